@@ -1,0 +1,225 @@
+/*
+ * pkv.h -- C ABI of libpkv: attention over a flat, slot-addressed KV pool
+ * (page_size = 1) on AMD Instinct MI355X (gfx950).
+ *
+ * Data model (AstrAI "Inference" guide, section "KVCache System"):
+ *   k_buffer, v_buffer   [n_layers, size, n_kv_heads, head_dim], one dtype
+ *   req_to_token         int32 [num_reqs, max_ctx_len]: logical position ->
+ *                        physical slot of the pool (one-token pages)
+ *   per step             req_pool_indices[B], seq_lens[B], kv_indptr[B+1],
+ *                        qo_indptr[B+1], out_cache_loc[n_new], host max_len
+ * Cached keys are already rotated: RoPE happens before the cache write
+ * (same guide, section "KV Cache"), so no kernel here rotates anything.
+ * All index arrays are int32 (commit history of tests/inference/test_cache.py,
+ * entry on int32 page-table, request-row and cache-location indices).
+ *
+ * Conventions for every entry point:
+ *   - "device" pointers are HIP device memory of the current device; "host"
+ *     pointers are ordinary CPU memory.  The caller owns every buffer.
+ *   - The library never allocates or frees device memory, never synchronises
+ *     the device, and keeps no state between calls except cached device
+ *     properties; calls are re-entrant and thread-safe.
+ *   - Kernels are enqueued on the caller's stream and return before they run.
+ *   - Host-checkable arguments are validated and reported as a pkv_status;
+ *     nothing is launched when a check fails.  Device-resident metadata is
+ *     NOT read on the host: inconsistent metadata (out-of-range slots, wrong
+ *     prefix sums) is undefined behaviour unless pkv_validate_step accepted
+ *     a host copy of it first.
+ *   - Offsets into the pool are computed in 64-bit arithmetic.
+ *   - Supported: head_dim 64 or 128; dtype f32 or bf16 (prefill: bf16 only);
+ *     n_heads a multiple of n_kv_heads.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,                 /* a required pointer is NULL            */
+  PKV_ERR_SHAPE = 2,                /* a size / count / layer out of range   */
+  PKV_ERR_DTYPE = 3,                /* dtype unsupported for this call       */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 4,  /* workspace below the required size     */
+  PKV_ERR_BAD_METADATA = 5,         /* pkv_validate_step / pkv_build_step    */
+  PKV_ERR_HIP = 6,                  /* a HIP runtime call or launch failed   */
+  PKV_ERR_UNSUPPORTED = 7           /* valid but not implemented (head_dim)  */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* KVStorage + ReqToTokenPool ("Inference" guide, section "KVCache System"). */
+typedef struct {
+  void *k_buffer;               /* device, [n_layers, size, n_kv_heads, head_dim] */
+  void *v_buffer;               /* device, same shape and dtype                   */
+  const int32_t *req_to_token;  /* device, [num_reqs, max_ctx_len], row-major     */
+  int64_t n_layers;
+  int64_t size;                 /* slots per layer                                */
+  int64_t num_reqs;
+  int64_t max_ctx_len;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  pkv_dtype dtype;
+} pkv_pool;
+
+/* One step's KVCache metadata (same section).  Arrays are device pointers;
+ * n_new, max_len and max_q_len are host values (max_len exists so that no
+ * device->host read is needed to size the decode launch). */
+typedef struct {
+  int32_t batch;
+  const int32_t *req_pool_indices;  /* [batch] row of req_to_token per request        */
+  const int32_t *seq_lens;          /* [batch] context length incl. this step's tokens */
+  const int32_t *kv_indptr;         /* [batch+1] exclusive prefix sum of seq_lens      */
+  const int32_t *qo_indptr;         /* [batch+1] exclusive prefix sum of q_lens; decode may pass NULL */
+  const int32_t *out_cache_loc;     /* [n_new] write slots in qo order                 */
+  int64_t n_new;                    /* total new tokens (decode: batch)                */
+  int32_t max_len;                  /* max(seq_lens)                                   */
+  int32_t max_q_len;                /* max(q_lens) (decode: 1)                         */
+} pkv_step;
+
+/* Human-readable name of a status. Never NULL. */
+const char *pkv_status_string(pkv_status s);
+
+/* hipError_t of the most recent PKV_ERR_HIP returned on the calling thread. */
+int32_t pkv_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * Step metadata, host side ("Inference" guide, section "KVCache System":
+ * kv_indptr and qo_indptr are prefix sums of seq_lens and of the per-request
+ * new-token counts, computed once per step; out_cache_loc holds the write
+ * slots of the forward; max_len = max(seq_lens)).
+ *
+ * All pointers are HOST memory.  Inputs: batch requests with table rows
+ * req_pool_indices, context lengths seq_lens (this step's tokens included)
+ * and new-token counts q_lens (NULL means 1 each, i.e. decode); the host
+ * copy of req_to_token [num_reqs, max_ctx_len].  Request b's new tokens are
+ * its last q_len_b logical positions, so its t-th new token is written to
+ * req_to_token[r_b, seq_len_b - q_len_b + t].
+ * Outputs: kv_indptr[batch+1], qo_indptr[batch+1], out_cache_loc (capacity
+ * out_cache_loc_cap entries, filled in qo order), *n_new, *max_len,
+ * *max_q_len.  Returns PKV_ERR_BAD_METADATA (outputs unspecified) when a
+ * row, length or new-token count is out of range, PKV_ERR_SHAPE when
+ * out_cache_loc_cap is too small.
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices,
+                          const int32_t *seq_lens, const int32_t *q_lens,
+                          const int32_t *req_to_token, int64_t num_reqs,
+                          int64_t max_ctx_len, int32_t *kv_indptr,
+                          int32_t *qo_indptr, int32_t *out_cache_loc,
+                          int64_t out_cache_loc_cap, int64_t *n_new,
+                          int32_t *max_len, int32_t *max_q_len);
+
+/* Checked mode: validates HOST copies of one step's metadata against a pool
+ * of `size` slots.  Accepts (PKV_OK) iff every request row is in
+ * [0, num_reqs), every seq_len in [1, max_ctx_len], every q_len in
+ * [0, seq_len], kv_indptr / qo_indptr are the exclusive prefix sums of the
+ * lengths (qo_indptr NULL means decode: q_len 1 each), every slot read
+ * (req_to_token[r_b, 0 .. seq_len_b-1]) lies in [0, size), the write slots
+ * are pairwise distinct, in [0, size), and equal the table entry of their
+ * token's logical position.  Else PKV_ERR_BAD_METADATA. */
+pkv_status pkv_validate_step(int64_t size, int64_t num_reqs, int64_t max_ctx_len,
+                             const int32_t *req_to_token, int32_t batch,
+                             const int32_t *req_pool_indices, const int32_t *seq_lens,
+                             const int32_t *kv_indptr, const int32_t *qo_indptr,
+                             const int32_t *out_cache_loc, int64_t n_new);
+
+/* ------------------------------------------------------------------------
+ * K/V write ("Inference" guide, section "KVCache System": the attention layer
+ * stores this forward's keys with k_buffer[layer_id, out_cache_loc] = k, and
+ * likewise v; section "Attention Backend": both backends write before they
+ * attend).
+ *
+ * k_new, v_new: device, [n_new, n_kv_heads, head_dim], pool dtype.
+ * out_cache_loc: device int32 [n_new], pairwise distinct slots in [0, size).
+ * Row i of k_new / v_new is copied bit for bit to slot out_cache_loc[i] of
+ * layer layer_id; no other byte of the pool changes.  n_new == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_kv_store(const pkv_pool *pool, int32_t layer_id, const void *k_new,
+                        const void *v_new, const int32_t *out_cache_loc, int64_t n_new,
+                        void *stream /* hipStream_t */);
+
+/* ------------------------------------------------------------------------
+ * Decode workspace (commit history of tests/inference/test_cache.py: the
+ * per-split partial outputs and (max, sum) pairs live in buffers the caller
+ * allocates once and passes to every step).
+ *
+ * Bytes needed by pkv_paged_decode / pkv_paged_decode_merge for up to
+ * max_batch requests, n_heads query heads and num_splits splits.  Layout
+ * (internal, documented for debugging): o_part fp32 [batch, n_heads,
+ * num_splits, head_dim], then ml_part fp32 [batch, n_heads, num_splits, 2]
+ * holding (m, l): m = running max of the base-2 scaled score
+ * (score * sm_scale * log2 e), l = sum of 2^(scaled score - m); o_part is
+ * normalised by l.  Empty splits hold (-inf, 0) and o = 0.
+ * Returns 0 for non-positive arguments.
+ * ---------------------------------------------------------------------- */
+size_t pkv_decode_workspace_bytes(int32_t max_batch, int32_t n_heads, int32_t head_dim,
+                                  int32_t num_splits);
+
+/* Host-only split-count heuristic (no device access, no sync): picks the
+ * number of KV splits for a decode launch from batch, n_kv_heads and the host
+ * max_len so that the launch fills the device, capped at max_splits (>= 1). */
+int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_heads,
+                               int32_t max_len, int32_t max_splits);
+
+/* ------------------------------------------------------------------------
+ * Split-KV paged decode ("Inference" guide, section "KV Cache": the single
+ * new query row of each request attends over all its cached keys,
+ * o = sum_j softmax(q . k_j * sm_scale) v_j; section "Attention Backend":
+ * req_to_token is the page table with one-token pages and the kernel gathers
+ * K/V itself; commit history of tests/inference/test_cache.py: per-split
+ * partial outputs in a caller-owned workspace).
+ *
+ * q: device [batch, n_heads, head_dim], pool dtype.  Query head h reads
+ * kv-head h / (n_heads / n_kv_heads).  Request b attends to logical keys
+ * 0 .. seq_lens[b]-1 (the token written this step included; write it with
+ * pkv_kv_store first) of layer layer_id.  Keys are split into num_splits
+ * contiguous logical ranges of ceil(max_len / num_splits) tokens (rounded up
+ * to a multiple of 16); each split's (m, l, o) partial goes to the workspace
+ * (layout above).  Call pkv_paged_decode_merge to form the output.
+ * Errors: PKV_ERR_WORKSPACE_TOO_SMALL when ws_bytes <
+ * pkv_decode_workspace_bytes(batch, n_heads, head_dim, num_splits).
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_paged_decode(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,
+                            const void *q, int32_t n_heads, float sm_scale,
+                            int32_t num_splits, void *workspace, size_t ws_bytes,
+                            void *stream /* hipStream_t */);
+
+/* Merge of the split partials written by pkv_paged_decode with the same
+ * batch, n_heads, head_dim and num_splits (same commit history entry): with
+ * M = max_s m_s and w_s = l_s 2^(m_s - M), out = sum_s w_s o_s / sum_s w_s;
+ * empty splits weigh 0.  out: device [batch, n_heads, head_dim] in out_dtype
+ * (bf16 rounded to nearest even). */
+pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_dim,
+                                  pkv_dtype out_dtype, int32_t num_splits,
+                                  const void *workspace, size_t ws_bytes, void *out,
+                                  void *stream /* hipStream_t */);
+
+/* ------------------------------------------------------------------------
+ * Ragged paged prefill ("Inference" guide, section "Attention Backend": after
+ * the K/V write, a ragged-batch kernel reads K/V straight from the flat pool
+ * through req_to_token, with each request's query and key counts taken from
+ * qo_indptr and kv_indptr).
+ *
+ * q, out: device [n_new, n_heads, head_dim] bf16, packed in qo order.
+ * Request i owns query rows qo_indptr[i] .. qo_indptr[i+1]-1 and
+ * kv_len_i = kv_indptr[i+1] - kv_indptr[i] keys; its t-th new token sits at
+ * logical position p_i + t with p_i = kv_len_i - q_len_i.  With causal != 0
+ * that token attends keys 0 .. p_i + t (mask aligned to the end of the
+ * context); with causal == 0 it attends all kv_len_i keys.  QK^T and PV run
+ * as bf16 matrix-core tiles with fp32 accumulation; the softmax weights are
+ * rounded to bf16 before the PV product.  Uses step->max_q_len (host) to
+ * size the launch.  Only PKV_BF16 pools are accepted (else PKV_ERR_DTYPE).
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,
+                             const void *q, int32_t n_heads, float sm_scale,
+                             int32_t causal, void *out, void *stream /* hipStream_t */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,81 @@
+"""Convenience layer over the C entry points: one step's metadata on the
+device, and the decode / prefill step sequences (write, attend, merge).
+Marshalling only: every stage runs in libpkv's kernels."""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import binding as B
+
+
+class DeviceStep:
+    """Metadata of one step, built on the host by pkv_build_step and copied to
+    the device once (int32 kv_indptr, qo_indptr, out_cache_loc, plus the
+    request rows and lengths), with the host scalars kept alongside."""
+
+    def __init__(self, req_pool_indices, seq_lens, req_to_token_host, q_lens=None,
+                 device="cuda"):
+        import torch
+        md = B.pkv_build_step(req_pool_indices, seq_lens, req_to_token_host, q_lens)
+        self.host = md
+        self.batch = len(md["kv_indptr"]) - 1
+        self.n_new = md["n_new"]
+        self.max_len = md["max_len"]
+        self.max_q_len = md["max_q_len"]
+        self.decode = q_lens is None
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+        self.req_pool_indices = to(B._host_i32(req_pool_indices, "req_pool_indices"))
+        self.seq_lens = to(B._host_i32(seq_lens, "seq_lens"))
+        self.kv_indptr = to(md["kv_indptr"])
+        self.qo_indptr = to(md["qo_indptr"])
+        self.out_cache_loc = to(md["out_cache_loc"]) if self.n_new else \
+            torch.zeros(0, dtype=torch.int32, device=device)
+        self.c = B.make_step(self.batch, self.req_pool_indices, self.seq_lens, self.kv_indptr,
+                             None if self.decode else self.qo_indptr,
+                             self.out_cache_loc if self.n_new else None, self.n_new,
+                             self.max_len, self.max_q_len)
+
+
+def decode_workspace(batch: int, n_heads: int, head_dim: int, num_splits: int, device="cuda"):
+    import torch
+    nbytes = B.pkv_decode_workspace_bytes(batch, n_heads, head_dim, num_splits)
+    return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=device)
+
+
+def decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q, k_new,
+                v_new, sm_scale: float, num_splits: Optional[int] = None, workspace=None,
+                out=None, write_kv: bool = True):
+    """K/V write of the step's new tokens, split decode, merge.  Returns out."""
+    import torch
+    H, d = int(q.shape[1]), int(q.shape[2])
+    if num_splits is None:
+        num_splits = B.pkv_decode_pick_splits(step.batch, int(k_buffer.shape[2]), H,
+                                              step.max_len)
+    if workspace is None:
+        workspace = decode_workspace(step.batch, H, d, num_splits, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if write_kv:
+        B.pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id, k_new, v_new,
+                       step.out_cache_loc)
+    B.pkv_paged_decode(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, sm_scale,
+                       num_splits, workspace)
+    B.pkv_paged_decode_merge(step.batch, H, d, num_splits, workspace, out)
+    return out
+
+
+def prefill_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q, k_new,
+                 v_new, sm_scale: float, causal: bool = True, out=None, write_kv: bool = True):
+    """K/V write of the step's new tokens, then ragged paged prefill."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    if write_kv:
+        B.pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id, k_new, v_new,
+                       step.out_cache_loc)
+    B.pkv_paged_prefill(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, sm_scale,
+                        causal, out)
+    return out

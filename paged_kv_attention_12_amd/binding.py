@@ -1,0 +1,301 @@
+"""ctypes binding of libpkv (include/pkv.h): argument marshalling only.
+
+Functions carry the C names.  Device arrays are torch tensors on the current
+HIP device (their data_ptr() is passed); host arrays are numpy arrays or
+CPU tensors.  Kernels are enqueued on torch's current stream.  Every non-OK
+status raises PkvError.  There is no fallback: if libpkv.so is missing, the
+first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_NULL = 1
+PKV_ERR_SHAPE = 2
+PKV_ERR_DTYPE = 3
+PKV_ERR_WORKSPACE_TOO_SMALL = 4
+PKV_ERR_BAD_METADATA = 5
+PKV_ERR_HIP = 6
+PKV_ERR_UNSUPPORTED = 7
+
+PKV_F32 = 0
+PKV_BF16 = 1
+
+EXPORTED = (
+    "pkv_status_string", "pkv_last_hip_error", "pkv_build_step", "pkv_validate_step",
+    "pkv_kv_store", "pkv_decode_workspace_bytes", "pkv_decode_pick_splits",
+    "pkv_paged_decode", "pkv_paged_decode_merge", "pkv_paged_prefill",
+)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class pkv_pool(C.Structure):
+    _fields_ = [
+        ("k_buffer", C.c_void_p), ("v_buffer", C.c_void_p), ("req_to_token", C.c_void_p),
+        ("n_layers", C.c_int64), ("size", C.c_int64), ("num_reqs", C.c_int64),
+        ("max_ctx_len", C.c_int64), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+        ("dtype", C.c_int32),
+    ]
+
+
+class pkv_step(C.Structure):
+    _fields_ = [
+        ("batch", C.c_int32), ("req_pool_indices", C.c_void_p), ("seq_lens", C.c_void_p),
+        ("kv_indptr", C.c_void_p), ("qo_indptr", C.c_void_p), ("out_cache_loc", C.c_void_p),
+        ("n_new", C.c_int64), ("max_len", C.c_int32), ("max_q_len", C.c_int32),
+    ]
+
+
+_lib: Optional[C.CDLL] = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> C.CDLL:
+    """Load libpkv.so (built in-tree by paged_kv_attention_12_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libpkv.so not built at {_LIB_PATH}; run "
+                          "`python -m paged_kv_attention_12_amd.build`")
+    lib = C.CDLL(_LIB_PATH)
+    P = C.c_void_p
+    i32, i64, f32, sz = C.c_int32, C.c_int64, C.c_float, C.c_size_t
+    sig = {
+        "pkv_status_string": (C.c_char_p, [C.c_int]),
+        "pkv_last_hip_error": (i32, []),
+        "pkv_build_step": (C.c_int, [i32, P, P, P, P, i64, i64, P, P, P, i64, P, P, P]),
+        "pkv_validate_step": (C.c_int, [i64, i64, i64, P, i32, P, P, P, P, P, i64]),
+        "pkv_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, P, i64, P]),
+        "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "pkv_decode_pick_splits": (i32, [i32, i32, i32, i32, i32]),
+        "pkv_paged_decode": (C.c_int, [C.POINTER(pkv_pool), i32, C.POINTER(pkv_step), P, i32,
+                                       f32, i32, P, sz, P]),
+        "pkv_paged_decode_merge": (C.c_int, [i32, i32, i32, C.c_int, i32, P, sz, P, P]),
+        "pkv_paged_prefill": (C.c_int, [C.POINTER(pkv_pool), i32, C.POINTER(pkv_step), P, i32,
+                                        f32, i32, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().pkv_status_string(int(status)).decode()
+    except ImportError:
+        return "?"
+
+
+def _check(status: int, what: str) -> None:
+    if status != PKV_OK:
+        raise PkvError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _dev_ptr(t, name: str, dtype=None) -> int:
+    import torch
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _host_i32(x, name: str) -> np.ndarray:
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        if x.is_cuda:
+            raise TypeError(f"{name} must be host memory")
+        x = x.detach().numpy()
+    a = np.ascontiguousarray(np.asarray(x), dtype=np.int32)
+    return a
+
+
+def _hp(a: Optional[np.ndarray]) -> int:
+    return 0 if a is None else a.ctypes.data
+
+
+def _stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_pool(k_buffer, v_buffer, req_to_token) -> pkv_pool:
+    """pkv_pool view of device tensors k_buffer / v_buffer [n_layers, size,
+    n_kv_heads, head_dim] and req_to_token int32 [num_reqs, max_ctx_len]."""
+    import torch
+    if k_buffer.shape != v_buffer.shape or k_buffer.dtype != v_buffer.dtype:
+        raise ValueError("k_buffer and v_buffer differ in shape or dtype")
+    if k_buffer.dim() != 4 or req_to_token.dim() != 2:
+        raise ValueError("pool must be 4-D and req_to_token 2-D")
+    p = pkv_pool()
+    p.k_buffer = _dev_ptr(k_buffer, "k_buffer")
+    p.v_buffer = _dev_ptr(v_buffer, "v_buffer")
+    p.req_to_token = _dev_ptr(req_to_token, "req_to_token", torch.int32)
+    p.n_layers, p.size, p.n_kv_heads, p.head_dim = (int(s) for s in k_buffer.shape)
+    p.num_reqs, p.max_ctx_len = (int(s) for s in req_to_token.shape)
+    p.dtype = dtype_code(k_buffer)
+    return p
+
+
+def make_step(batch: int, req_pool_indices, seq_lens, kv_indptr=None, qo_indptr=None,
+              out_cache_loc=None, n_new: Optional[int] = None, max_len: int = 0,
+              max_q_len: int = 1) -> pkv_step:
+    """pkv_step view of device int32 tensors plus the host scalars."""
+    import torch
+    s = pkv_step()
+    s.batch = int(batch)
+    s.req_pool_indices = _dev_ptr(req_pool_indices, "req_pool_indices", torch.int32)
+    s.seq_lens = _dev_ptr(seq_lens, "seq_lens", torch.int32)
+    s.kv_indptr = _dev_ptr(kv_indptr, "kv_indptr", torch.int32)
+    s.qo_indptr = _dev_ptr(qo_indptr, "qo_indptr", torch.int32)
+    s.out_cache_loc = _dev_ptr(out_cache_loc, "out_cache_loc", torch.int32)
+    s.n_new = int(batch if n_new is None else n_new)
+    s.max_len = int(max_len)
+    s.max_q_len = int(max_q_len)
+    return s
+
+
+# ---------------------------------------------------------------------------
+# entry points (C names)
+# ---------------------------------------------------------------------------
+def pkv_build_step(req_pool_indices, seq_lens, req_to_token, q_lens=None) -> dict:
+    """Host step metadata: returns dict of int32 numpy arrays kv_indptr,
+    qo_indptr, out_cache_loc and ints n_new, max_len, max_q_len."""
+    rpi = _host_i32(req_pool_indices, "req_pool_indices")
+    sl = _host_i32(seq_lens, "seq_lens")
+    ql = _host_i32(q_lens, "q_lens")
+    table = _host_i32(req_to_token, "req_to_token")
+    if table.ndim != 2:
+        raise ValueError("req_to_token must be 2-D")
+    B = len(sl)
+    if len(rpi) != B or (ql is not None and len(ql) != B):
+        raise ValueError("batch arrays differ in length")
+    cap = int(ql.sum()) if ql is not None else B
+    kv = np.zeros(B + 1, dtype=np.int32)
+    qo = np.zeros(B + 1, dtype=np.int32)
+    loc = np.zeros(max(cap, 1), dtype=np.int32)
+    n_new, ml, mq = C.c_int64(0), C.c_int32(0), C.c_int32(0)
+    st = load().pkv_build_step(B, _hp(rpi), _hp(sl), _hp(ql), _hp(table), table.shape[0],
+                               table.shape[1], _hp(kv), _hp(qo), _hp(loc), cap,
+                               C.byref(n_new), C.byref(ml), C.byref(mq))
+    _check(st, "pkv_build_step")
+    return {"kv_indptr": kv, "qo_indptr": qo, "out_cache_loc": loc[:n_new.value].copy(),
+            "n_new": n_new.value, "max_len": ml.value, "max_q_len": mq.value}
+
+
+def pkv_validate_step(size: int, req_to_token, req_pool_indices, seq_lens, kv_indptr,
+                      qo_indptr, out_cache_loc) -> int:
+    """Checked mode on host copies; returns the status (0 = well formed)."""
+    table = _host_i32(req_to_token, "req_to_token")
+    rpi = _host_i32(req_pool_indices, "req_pool_indices")
+    sl = _host_i32(seq_lens, "seq_lens")
+    kv = _host_i32(kv_indptr, "kv_indptr")
+    qo = _host_i32(qo_indptr, "qo_indptr")
+    loc = _host_i32(out_cache_loc, "out_cache_loc")
+    B = len(sl)
+    if len(rpi) != B or len(kv) != B + 1 or (qo is not None and len(qo) != B + 1):
+        return PKV_ERR_BAD_METADATA
+    return int(load().pkv_validate_step(int(size), table.shape[0], table.shape[1], _hp(table),
+                                        B, _hp(rpi), _hp(sl), _hp(kv), _hp(qo), _hp(loc),
+                                        0 if loc is None else len(loc)))
+
+
+def pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, k_new, v_new,
+                 out_cache_loc) -> None:
+    import torch
+    pool = make_pool(k_buffer, v_buffer, req_to_token)
+    n_new = int(out_cache_loc.numel())
+    if n_new and (k_new.shape[0] != n_new or v_new.shape[0] != n_new
+                  or tuple(k_new.shape[1:]) != tuple(k_buffer.shape[2:])
+                  or k_new.shape != v_new.shape or k_new.dtype != k_buffer.dtype
+                  or v_new.dtype != k_buffer.dtype):
+        raise ValueError("k_new / v_new must be [n_new, n_kv_heads, head_dim] in the pool dtype")
+    st = load().pkv_kv_store(C.byref(pool), int(layer_id),
+                             _dev_ptr(k_new, "k_new") if n_new else 0,
+                             _dev_ptr(v_new, "v_new") if n_new else 0,
+                             _dev_ptr(out_cache_loc, "out_cache_loc", torch.int32) if n_new else 0,
+                             n_new, _stream())
+    _check(st, "pkv_kv_store")
+
+
+def pkv_decode_workspace_bytes(max_batch: int, n_heads: int, head_dim: int,
+                               num_splits: int) -> int:
+    return int(load().pkv_decode_workspace_bytes(max_batch, n_heads, head_dim, num_splits))
+
+
+def pkv_decode_pick_splits(batch: int, n_kv_heads: int, n_heads: int, max_len: int,
+                           max_splits: int = 1024) -> int:
+    return int(load().pkv_decode_pick_splits(batch, n_kv_heads, n_heads, max_len, max_splits))
+
+
+def pkv_paged_decode(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,
+                     sm_scale: float, num_splits: int, workspace) -> None:
+    pool = make_pool(k_buffer, v_buffer, req_to_token)
+    if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
+            or q.dtype != k_buffer.dtype:
+        raise ValueError("q must be [batch, n_heads, head_dim] in the pool dtype")
+    st = load().pkv_paged_decode(C.byref(pool), int(layer_id), C.byref(step),
+                                 _dev_ptr(q, "q"), int(q.shape[1]), float(sm_scale),
+                                 int(num_splits), _dev_ptr(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream())
+    _check(st, "pkv_paged_decode")
+
+
+def pkv_paged_decode_merge(batch: int, n_heads: int, head_dim: int, num_splits: int,
+                           workspace, out) -> None:
+    if out.dim() != 3 or tuple(out.shape) != (batch, n_heads, head_dim):
+        raise ValueError("out must be [batch, n_heads, head_dim]")
+    st = load().pkv_paged_decode_merge(int(batch), int(n_heads), int(head_dim), dtype_code(out),
+                                       int(num_splits), _dev_ptr(workspace, "workspace"),
+                                       workspace.numel() * workspace.element_size(),
+                                       _dev_ptr(out, "out"), _stream())
+    _check(st, "pkv_paged_decode_merge")
+
+
+def pkv_paged_prefill(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,
+                      sm_scale: float, causal: bool, out) -> None:
+    pool = make_pool(k_buffer, v_buffer, req_to_token)
+    if q.dim() != 3 or q.shape[0] != step.n_new or q.shape[2] != k_buffer.shape[3] \
+            or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q / out must be [n_new, n_heads, head_dim] in the pool dtype")
+    st = load().pkv_paged_prefill(C.byref(pool), int(layer_id), C.byref(step), _dev_ptr(q, "q"),
+                                  int(q.shape[1]), float(sm_scale), 1 if causal else 0,
+                                  _dev_ptr(out, "out"), _stream())
+    _check(st, "pkv_paged_prefill")

@@ -1,0 +1,67 @@
+// Device-side helpers shared by the libpkv kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// bf16 values are carried as raw 16-bit patterns; two of them share a dword.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bit pattern, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c with bf16 pairs held in dwords (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// 2^x on the transcendental unit; 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane permutations inside a row of 16 lanes.
+enum : int {
+  DPP_QUAD_XOR1 = 0xB1,      // quad_perm [1,0,3,2]
+  DPP_QUAD_XOR2 = 0x4E,      // quad_perm [2,3,0,1]
+  DPP_ROW_MIRROR = 0x140,    // lane i <- lane 15-i
+  DPP_ROW_HALF_MIRROR = 0x141  // lane i <- lane 7-i within each half row
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N in {4, 8, 16, 32, 64}); every lane of
+// a group receives the group total.  Groups up to 16 use DPP only.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  x += dpp_f32<DPP_QUAD_XOR1>(x);
+  x += dpp_f32<DPP_QUAD_XOR2>(x);
+  if constexpr (N >= 8) x += dpp_f32<DPP_ROW_HALF_MIRROR>(x);
+  if constexpr (N >= 16) x += dpp_f32<DPP_ROW_MIRROR>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ uint4 load16(const void *p) {
+  return *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ void store16(void *p, uint4 v) {
+  *reinterpret_cast<uint4 *>(p) = v;
+}
+
+}  // namespace pkv

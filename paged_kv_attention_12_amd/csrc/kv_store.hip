@@ -1,0 +1,48 @@
+// K/V write of one forward into the flat pool: row i of k_new / v_new goes to
+// slot out_cache_loc[i] of the layer (AstrAI "Inference" guide, section
+// "KVCache System", raw-index write; section "Attention Backend", the write
+// precedes attention).  A bitwise copy: HBM-bound, 2 * n_new * row_bytes read
+// and as much written.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace pkv {
+
+// One thread moves one W-byte piece of a K row and the same piece of the V
+// row.  Consecutive threads cover consecutive pieces of a row, so each row is
+// read and written as one contiguous, fully coalesced run.
+template <typename W>
+__global__ void __launch_bounds__(256) kv_store_kernel(KvStoreArgs a, int64_t total_pieces,
+                                                       int32_t pieces_per_row) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= total_pieces) return;
+  const int64_t i = t / pieces_per_row;
+  const int32_t c = (int32_t)(t - i * pieces_per_row);
+  const int64_t loc = a.out_cache_loc[i];
+  const int64_t src = i * pieces_per_row + c;
+  const int64_t dst = loc * pieces_per_row + c;
+  const W kx = reinterpret_cast<const W *>(a.k_new)[src];
+  const W vx = reinterpret_cast<const W *>(a.v_new)[src];
+  reinterpret_cast<W *>(a.k_layer)[dst] = kx;
+  reinterpret_cast<W *>(a.v_layer)[dst] = vx;
+}
+
+hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t stream) {
+  if (a.n_new == 0) return hipSuccess;
+  const int threads = 256;
+  auto go = [&](auto tag, int width) {
+    using W = decltype(tag);
+    const int32_t ppr = a.row_bytes / width;
+    const int64_t total = a.n_new * ppr;
+    const int64_t blocks = (total + threads - 1) / threads;
+    hipLaunchKernelGGL(kv_store_kernel<W>, dim3((uint32_t)blocks), dim3(threads), 0, stream, a,
+                       total, ppr);
+    return hipGetLastError();
+  };
+  if (a.row_bytes % 16 == 0) return go(uint4{}, 16);
+  if (a.row_bytes % 8 == 0) return go(uint2{}, 8);
+  if (a.row_bytes % 4 == 0) return go(uint32_t{}, 4);
+  return go(uint16_t{}, 2);
+}
+
+}  // namespace pkv

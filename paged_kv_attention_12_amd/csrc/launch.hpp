@@ -1,0 +1,74 @@
+// Internal launch interface between the C ABI (pkv_api.cpp) and the kernels.
+// Arguments here are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct KvStoreArgs {
+  void *k_layer;              // k_buffer + layer_id * size * row_elems (bytes as char*)
+  void *v_layer;
+  const void *k_new;          // [n_new, row_bytes]
+  const void *v_new;
+  const int32_t *out_cache_loc;
+  int64_t n_new;
+  int64_t size;
+  int32_t row_bytes;          // n_kv_heads * head_dim * sizeof(dtype)
+};
+hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void *k_layer;        // first element of layer layer_id
+  const void *v_layer;
+  const int32_t *req_to_token;
+  int64_t max_ctx_len;
+  const int32_t *req_pool_indices;
+  const int32_t *seq_lens;
+  const void *q;              // [batch, n_heads, head_dim]
+  float *o_part;              // [batch, n_heads, num_splits, head_dim]
+  float *ml_part;             // [batch, n_heads, num_splits, 2]
+  int32_t batch;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t group;              // n_heads / n_kv_heads
+  int32_t n_chunks;           // head chunks per kv-head (group split into chunks of <= 8)
+  int32_t heads_per_chunk;
+  int32_t num_splits;
+  int32_t chunk;              // tokens per split (multiple of 16)
+  float scale_log2;           // sm_scale * log2(e)
+};
+// dtype: 0 = f32, 1 = bf16
+hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
+
+struct MergeArgs {
+  const float *o_part;
+  const float *ml_part;
+  void *out;                  // [batch, n_heads, head_dim]
+  int32_t rows;               // batch * n_heads
+  int32_t num_splits;
+};
+hipError_t launch_decode_merge(const MergeArgs &a, int dtype, int head_dim, hipStream_t stream);
+
+struct PrefillArgs {
+  const void *k_layer;
+  const void *v_layer;
+  const int32_t *req_to_token;
+  int64_t max_ctx_len;
+  const int32_t *req_pool_indices;
+  const int32_t *qo_indptr;
+  const int32_t *kv_indptr;
+  const void *q;              // [n_new, n_heads, head_dim] bf16
+  void *out;                  // [n_new, n_heads, head_dim] bf16
+  int32_t batch;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t group;
+  int32_t max_q_len;
+  int32_t causal;
+  float scale_log2;
+};
+hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, hipStream_t stream);
+
+}  // namespace pkv

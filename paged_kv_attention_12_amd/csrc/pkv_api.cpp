@@ -1,0 +1,288 @@
+// C ABI of libpkv: argument checks, workspace sizing, split choice and kernel
+// launches on the caller's stream.  Declarations and contracts: include/pkv.h.
+#include "../../include/pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <unordered_set>
+#include <vector>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+pkv_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return PKV_OK;
+  g_last_hip_error = (int32_t)e;
+  return PKV_ERR_HIP;
+}
+
+size_t dtype_bytes(pkv_dtype d) { return d == PKV_BF16 ? 2 : 4; }
+
+bool dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16; }
+
+// Token-range granularity of one split (rows per decode iteration divide it).
+constexpr int32_t kSplitAlign = 16;
+// Query heads one decode wavefront serves at most.
+constexpr int32_t kMaxHeadsPerWave = 8;
+
+pkv_status check_pool(const pkv_pool *p, int32_t layer_id) {
+  if (!p || !p->k_buffer || !p->v_buffer || !p->req_to_token) return PKV_ERR_NULL;
+  if (!dtype_ok(p->dtype)) return PKV_ERR_DTYPE;
+  if (p->n_layers <= 0 || p->size <= 0 || p->num_reqs <= 0 || p->max_ctx_len <= 0 ||
+      p->n_kv_heads <= 0 || p->head_dim <= 0)
+    return PKV_ERR_SHAPE;
+  if (p->size > INT32_MAX) return PKV_ERR_SHAPE;  // slots are int32
+  if (layer_id < 0 || layer_id >= p->n_layers) return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+const char *layer_ptr(const void *buf, const pkv_pool *p, int32_t layer_id) {
+  const int64_t row = (int64_t)p->n_kv_heads * p->head_dim * (int64_t)dtype_bytes(p->dtype);
+  return reinterpret_cast<const char *>(buf) + (int64_t)layer_id * p->size * row;
+}
+
+int32_t decode_chunk(int32_t max_len, int32_t num_splits) {
+  int64_t c = ((int64_t)max_len + num_splits - 1) / num_splits;
+  c = ((c + kSplitAlign - 1) / kSplitAlign) * kSplitAlign;
+  return (int32_t)std::max<int64_t>(c, kSplitAlign);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "null pointer argument";
+    case PKV_ERR_SHAPE: return "size, count or layer out of range";
+    case PKV_ERR_DTYPE: return "unsupported dtype";
+    case PKV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PKV_ERR_BAD_METADATA: return "inconsistent step metadata";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+int32_t pkv_last_hip_error(void) { return g_last_hip_error; }
+
+pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices, const int32_t *seq_lens,
+                          const int32_t *q_lens, const int32_t *req_to_token, int64_t num_reqs,
+                          int64_t max_ctx_len, int32_t *kv_indptr, int32_t *qo_indptr,
+                          int32_t *out_cache_loc, int64_t out_cache_loc_cap, int64_t *n_new,
+                          int32_t *max_len, int32_t *max_q_len) {
+  if (batch < 0) return PKV_ERR_SHAPE;
+  if (!kv_indptr || !qo_indptr || !n_new || !max_len || !max_q_len) return PKV_ERR_NULL;
+  if (batch > 0 && (!req_pool_indices || !seq_lens || !req_to_token)) return PKV_ERR_NULL;
+  int64_t kv = 0, qo = 0;
+  int32_t ml = 0, mq = 0;
+  kv_indptr[0] = 0;
+  qo_indptr[0] = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t r = req_pool_indices[b];
+    const int32_t L = seq_lens[b];
+    const int32_t ql = q_lens ? q_lens[b] : 1;
+    if (r < 0 || r >= num_reqs || L < 1 || L > max_ctx_len || ql < 0 || ql > L)
+      return PKV_ERR_BAD_METADATA;
+    kv += L;
+    if (kv > INT32_MAX) return PKV_ERR_BAD_METADATA;  // indptr entries are int32
+    kv_indptr[b + 1] = (int32_t)kv;
+    if (qo + ql > out_cache_loc_cap) return PKV_ERR_SHAPE;
+    if (ql > 0 && !out_cache_loc) return PKV_ERR_NULL;
+    const int32_t *row = req_to_token + r * max_ctx_len;
+    for (int32_t t = 0; t < ql; ++t) out_cache_loc[qo + t] = row[L - ql + t];
+    qo += ql;
+    qo_indptr[b + 1] = (int32_t)qo;
+    ml = std::max(ml, L);
+    mq = std::max(mq, ql);
+  }
+  *n_new = qo;
+  *max_len = ml;
+  *max_q_len = mq;
+  return PKV_OK;
+}
+
+pkv_status pkv_validate_step(int64_t size, int64_t num_reqs, int64_t max_ctx_len,
+                             const int32_t *req_to_token, int32_t batch,
+                             const int32_t *req_pool_indices, const int32_t *seq_lens,
+                             const int32_t *kv_indptr, const int32_t *qo_indptr,
+                             const int32_t *out_cache_loc, int64_t n_new) {
+  if (batch < 0 || size <= 0 || num_reqs <= 0 || max_ctx_len <= 0) return PKV_ERR_SHAPE;
+  if (batch == 0) return n_new == 0 ? PKV_OK : PKV_ERR_BAD_METADATA;
+  if (!req_to_token || !req_pool_indices || !seq_lens || !kv_indptr) return PKV_ERR_NULL;
+  if (n_new > 0 && !out_cache_loc) return PKV_ERR_NULL;
+  if (kv_indptr[0] != 0 || (qo_indptr && qo_indptr[0] != 0)) return PKV_ERR_BAD_METADATA;
+  const int64_t expect_new = qo_indptr ? qo_indptr[batch] : batch;
+  if (expect_new != n_new) return PKV_ERR_BAD_METADATA;
+  std::unordered_set<int32_t> seen;
+  seen.reserve((size_t)std::max<int64_t>(n_new, 0) * 2);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t r = req_pool_indices[b];
+    const int64_t L = seq_lens[b];
+    if (r < 0 || r >= num_reqs || L < 1 || L > max_ctx_len) return PKV_ERR_BAD_METADATA;
+    if ((int64_t)kv_indptr[b + 1] - kv_indptr[b] != L) return PKV_ERR_BAD_METADATA;
+    const int64_t q0 = qo_indptr ? qo_indptr[b] : b;
+    const int64_t ql = qo_indptr ? (int64_t)qo_indptr[b + 1] - qo_indptr[b] : 1;
+    if (ql < 0 || ql > L || q0 + ql > n_new) return PKV_ERR_BAD_METADATA;
+    const int32_t *row = req_to_token + r * max_ctx_len;
+    for (int64_t j = 0; j < L; ++j)
+      if (row[j] < 0 || row[j] >= size) return PKV_ERR_BAD_METADATA;
+    for (int64_t t = 0; t < ql; ++t) {
+      const int32_t loc = out_cache_loc[q0 + t];
+      if (loc < 0 || loc >= size) return PKV_ERR_BAD_METADATA;
+      if (!seen.insert(loc).second) return PKV_ERR_BAD_METADATA;
+      if (loc != row[L - ql + t]) return PKV_ERR_BAD_METADATA;
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_kv_store(const pkv_pool *pool, int32_t layer_id, const void *k_new,
+                        const void *v_new, const int32_t *out_cache_loc, int64_t n_new,
+                        void *stream) {
+  pkv_status st = check_pool(pool, layer_id);
+  if (st != PKV_OK) return st;
+  if (n_new < 0) return PKV_ERR_SHAPE;
+  if (n_new == 0) return PKV_OK;
+  if (!k_new || !v_new || !out_cache_loc) return PKV_ERR_NULL;
+  const int64_t row_bytes = (int64_t)pool->n_kv_heads * pool->head_dim * dtype_bytes(pool->dtype);
+  if (row_bytes > INT32_MAX) return PKV_ERR_SHAPE;
+  pkv::KvStoreArgs a;
+  a.k_layer = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
+  a.v_layer = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.out_cache_loc = out_cache_loc;
+  a.n_new = n_new;
+  a.size = pool->size;
+  a.row_bytes = (int32_t)row_bytes;
+  return hip_status(pkv::launch_kv_store(a, (hipStream_t)stream));
+}
+
+size_t pkv_decode_workspace_bytes(int32_t max_batch, int32_t n_heads, int32_t head_dim,
+                                  int32_t num_splits) {
+  if (max_batch <= 0 || n_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
+  const size_t rows = (size_t)max_batch * n_heads * num_splits;
+  const size_t o_bytes = rows * head_dim * sizeof(float);
+  const size_t ml_bytes = rows * 2 * sizeof(float);
+  return o_bytes + ml_bytes;
+}
+
+int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_heads,
+                               int32_t max_len, int32_t max_splits) {
+  if (batch <= 0 || n_kv_heads <= 0 || n_heads <= 0 || max_len <= 0) return 1;
+  max_splits = std::max(1, max_splits);
+  const int32_t group = std::max(1, n_heads / n_kv_heads);
+  const int32_t chunks = (group + kMaxHeadsPerWave - 1) / kMaxHeadsPerWave;
+  // Aim for about 4096 busy wavefronts (16 per CU on 256 CUs) while keeping
+  // at least 256 tokens per split so the per-split overhead stays small.
+  const int64_t waves_per_split = (int64_t)batch * n_kv_heads * chunks;
+  int64_t s = (4096 + waves_per_split - 1) / waves_per_split;
+  const int64_t by_len = std::max<int64_t>(1, ((int64_t)max_len + 255) / 256);
+  s = std::min(s, by_len);
+  s = std::min<int64_t>(s, max_splits);
+  return (int32_t)std::max<int64_t>(1, s);
+}
+
+pkv_status pkv_paged_decode(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,
+                            const void *q, int32_t n_heads, float sm_scale, int32_t num_splits,
+                            void *workspace, size_t ws_bytes, void *stream) {
+  pkv_status st = check_pool(pool, layer_id);
+  if (st != PKV_OK) return st;
+  if (!step || !q || !workspace) return PKV_ERR_NULL;
+  if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || num_splits <= 0 ||
+      num_splits > 65535 || step->batch > 65535)
+    return PKV_ERR_SHAPE;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(sm_scale)) return PKV_ERR_SHAPE;
+  if (step->batch == 0) return PKV_OK;
+  if (!step->req_pool_indices || !step->seq_lens) return PKV_ERR_NULL;
+  if (step->max_len <= 0 || step->max_len > pool->max_ctx_len) return PKV_ERR_SHAPE;
+  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, pool->head_dim, num_splits))
+    return PKV_ERR_WORKSPACE_TOO_SMALL;
+  const int32_t group = n_heads / pool->n_kv_heads;
+  const int32_t chunks = (group + kMaxHeadsPerWave - 1) / kMaxHeadsPerWave;
+  pkv::DecodeArgs a;
+  a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
+  a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
+  a.req_to_token = pool->req_to_token;
+  a.max_ctx_len = pool->max_ctx_len;
+  a.req_pool_indices = step->req_pool_indices;
+  a.seq_lens = step->seq_lens;
+  a.q = q;
+  a.o_part = reinterpret_cast<float *>(workspace);
+  a.ml_part = a.o_part + (size_t)step->batch * n_heads * num_splits * pool->head_dim;
+  a.batch = step->batch;
+  a.n_heads = n_heads;
+  a.n_kv_heads = pool->n_kv_heads;
+  a.group = group;
+  a.n_chunks = chunks;
+  a.heads_per_chunk = (group + chunks - 1) / chunks;
+  a.num_splits = num_splits;
+  a.chunk = decode_chunk(step->max_len, num_splits);
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  return hip_status(pkv::launch_paged_decode(a, pool->dtype == PKV_BF16 ? 1 : 0,
+                                              pool->head_dim, (hipStream_t)stream));
+}
+
+pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_dim,
+                                  pkv_dtype out_dtype, int32_t num_splits, const void *workspace,
+                                  size_t ws_bytes, void *out, void *stream) {
+  if (!workspace || !out) return PKV_ERR_NULL;
+  if (!dtype_ok(out_dtype)) return PKV_ERR_DTYPE;
+  if (batch < 0 || n_heads <= 0 || num_splits <= 0) return PKV_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (batch == 0) return PKV_OK;
+  if (ws_bytes < pkv_decode_workspace_bytes(batch, n_heads, head_dim, num_splits))
+    return PKV_ERR_WORKSPACE_TOO_SMALL;
+  pkv::MergeArgs a;
+  a.o_part = reinterpret_cast<const float *>(workspace);
+  a.ml_part = a.o_part + (size_t)batch * n_heads * num_splits * head_dim;
+  a.out = out;
+  a.rows = batch * n_heads;
+  a.num_splits = num_splits;
+  return hip_status(pkv::launch_decode_merge(a, out_dtype == PKV_BF16 ? 1 : 0, head_dim,
+                                             (hipStream_t)stream));
+}
+
+pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,
+                             const void *q, int32_t n_heads, float sm_scale, int32_t causal,
+                             void *out, void *stream) {
+  pkv_status st = check_pool(pool, layer_id);
+  if (st != PKV_OK) return st;
+  if (pool->dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (!step || !q || !out) return PKV_ERR_NULL;
+  if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || step->batch > 65535)
+    return PKV_ERR_SHAPE;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(sm_scale)) return PKV_ERR_SHAPE;
+  if (step->batch == 0 || step->n_new == 0) return PKV_OK;
+  if (!step->req_pool_indices || !step->qo_indptr || !step->kv_indptr) return PKV_ERR_NULL;
+  if (step->max_q_len <= 0 || step->max_q_len > pool->max_ctx_len) return PKV_ERR_SHAPE;
+  pkv::PrefillArgs a;
+  a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
+  a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
+  a.req_to_token = pool->req_to_token;
+  a.max_ctx_len = pool->max_ctx_len;
+  a.req_pool_indices = step->req_pool_indices;
+  a.qo_indptr = step->qo_indptr;
+  a.kv_indptr = step->kv_indptr;
+  a.q = q;
+  a.out = out;
+  a.batch = step->batch;
+  a.n_heads = n_heads;
+  a.n_kv_heads = pool->n_kv_heads;
+  a.group = n_heads / pool->n_kv_heads;
+  a.max_q_len = step->max_q_len;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  return hip_status(pkv::launch_paged_prefill(a, pool->head_dim, (hipStream_t)stream));
+}
+
+}  // extern "C"

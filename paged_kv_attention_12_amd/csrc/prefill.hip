@@ -1,0 +1,299 @@
+// Ragged causal paged prefill on bf16 matrix cores (gfx950).
+//
+// What is computed (AstrAI "Inference" guide, section "Attention Backend"):
+// after this forward's K/V are written, request i's q_len_i new tokens attend
+// over its kv_len_i keys, read straight from the flat pool through
+// req_to_token; q_len_i and kv_len_i come from qo_indptr and kv_indptr.  The
+// t-th new token sits at logical position p_i + t, p_i = kv_len_i - q_len_i,
+// and with the causal mask it sees keys 0 .. p_i + t.  Each output row is
+// o = sum_j softmax_j(q . k_j * sm_scale) v_j (section "KV Cache").
+//
+// Tiling.  A workgroup (4 wavefronts) owns one (request, kv-head, block of 128
+// query rows), where the rows of a request enumerate (token t, head g of the
+// kv-head's group) as r = t * G + g, so all G query heads sharing a kv-head
+// reuse one K/V tile and any group size works.  Each wavefront owns 32 rows.
+// Keys stream through LDS in tiles of 64, gathered by slot:
+//   S^T (keys x rows) = K Q^T : v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
+//                               B = the wave's Q rows held in registers;
+//   O^T (dims x rows) += V^T P^T : A = V^T from LDS (V is stored transposed),
+//                               B = the softmax weights, rounded to bf16,
+//                               taken straight from the S^T accumulators.
+// With S^T in this orientation every lane holds one query row, so the
+// online-softmax row max / row sum need one cross-lane step (lane l ^ 32).
+// The next tile's K/V rows are fetched into registers while the current tile
+// is being multiplied.
+#include <math.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace pkv {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr float kNegInf = -INFINITY;
+constexpr int BM = 128;   // query rows per workgroup
+constexpr int BN = 64;    // keys per tile
+constexpr int WROWS = 32; // query rows per wavefront
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ f32x16_t mfma32(const uint4 &a, const uint4 &b, const f32x16_t &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Position of key k of a 64-key tile inside a transposed V row: bits 2 and 3 of
+// the key index are swapped, so that the eight keys one lane feeds to a PV
+// product (keys 16t + {0..3, 8..11} or 16t + {4..7, 12..15}) are contiguous.
+__device__ __forceinline__ int vpos(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+template <int D>
+struct Smem {
+  static constexpr int KS = D + 8;   // K row stride (elements), 16-byte pad
+  static constexpr int VS = BN + 8;  // V^T row stride (elements), 16-byte pad
+  uint16_t k[BN * KS];
+  uint16_t vt[D * VS];
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
+  constexpr int KS = Smem<D>::KS;
+  constexpr int VS = Smem<D>::VS;
+  constexpr int KSTEPS = D / 16;      // MFMA steps over head_dim for S^T
+  constexpr int DBLK = D / 32;        // 32-dim blocks of O^T
+  constexpr int KPIECES = BN * D / 8 / 256;  // 16-byte K pieces per thread per tile
+  constexpr int VJOBS = (BN / 4) * (D / 8);  // (4-key, 8-dim) V jobs per tile
+  __shared__ Smem<D> sm;
+
+  const int i = blockIdx.z;
+  const int hk = blockIdx.y;
+  const int G = a.group;
+  const int q0 = a.qo_indptr[i];
+  const int q_len = a.qo_indptr[i + 1] - q0;
+  const int kv_len = a.kv_indptr[i + 1] - a.kv_indptr[i];
+  const int rows = q_len * G;
+  const int nblk = (rows + BM - 1) / BM;
+  if ((int)blockIdx.x >= nblk) return;
+  const int rb = nblk - 1 - (int)blockIdx.x;  // heaviest row block first
+  const int prefix = kv_len - q_len;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // This lane's query row (column of S^T / O^T).
+  const int r = rb * BM + wave * WROWS + col;
+  const bool row_ok = r < rows;
+  const int t = row_ok ? r / G : 0;
+  const int g = row_ok ? r - t * G : 0;
+  const int h = hk * G + g;
+  // Keys visible to this row.
+  const int lim = !row_ok ? 0 : (a.causal ? prefix + t + 1 : kv_len);
+
+  // Keys any row of the workgroup sees.
+  const int r_last = min(rows, (rb + 1) * BM) - 1;
+  const int kv_end = a.causal ? min(kv_len, prefix + r_last / G + 1) : kv_len;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  // Smallest per-row limit among this wave's valid rows: tiles wholly below it
+  // need no mask.
+  const int r_first = rb * BM + wave * WROWS;
+  const int wave_min_lim =
+      r_first >= rows ? 0 : (a.causal ? prefix + r_first / G + 1 : kv_len);
+
+  // Q (B operand of S^T): lane holds dims 16s + 8*half .. +8 of its row for step s.
+  uint4 qf[KSTEPS];
+  {
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) +
+                           ((int64_t)(q0 + t) * a.n_heads + h) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      qf[s] = row_ok ? load16(qrow + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  const int32_t *table = a.req_to_token + (int64_t)a.req_pool_indices[i] * a.max_ctx_len;
+  const int64_t row_elems = (int64_t)a.n_kv_heads * D;
+  const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k_layer) + (int64_t)hk * D;
+  const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v_layer) + (int64_t)hk * D;
+
+  // Global -> register staging of one tile.
+  uint4 kreg[KPIECES];
+  uint4 vreg[4];
+  const int vjob = tid;  // V job: keys 4*(vjob / (D/8)) .. +3, dims 8*(vjob % (D/8)) .. +7
+  const int vkq = vjob / (D / 8);
+  const int vdg = vjob - vkq * (D / 8);
+
+  auto fetch = [&](int tile) {
+    const int base = tile * BN;
+#pragma unroll
+    for (int p = 0; p < KPIECES; ++p) {
+      const int piece = tid + 256 * p;
+      const int key = piece / (D / 8);
+      const int dg = piece - key * (D / 8);
+      const int j = base + key;
+      kreg[p] = make_uint4(0u, 0u, 0u, 0u);
+      if (j < kv_end) kreg[p] = load16(kbase + (int64_t)table[j] * row_elems + dg * 8);
+    }
+    if (vjob < VJOBS) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = base + vkq * 4 + c;
+        vreg[c] = make_uint4(0u, 0u, 0u, 0u);
+        if (j < kv_end) vreg[c] = load16(vbase + (int64_t)table[j] * row_elems + vdg * 8);
+      }
+    }
+  };
+
+  auto stash = [&]() {
+#pragma unroll
+    for (int p = 0; p < KPIECES; ++p) {
+      const int piece = tid + 256 * p;
+      const int key = piece / (D / 8);
+      const int dg = piece - key * (D / 8);
+      store16(&sm.k[key * KS + dg * 8], kreg[p]);
+    }
+    if (vjob < VJOBS) {
+      // Transpose 4 keys x 8 dims: each dim becomes 4 contiguous keys.
+      const int pos = vpos(vkq * 4);
+      const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
+                                {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
+                                {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
+                                {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) ? 16 : 0;
+        const uint32_t k0 = (w[0][e >> 1] >> sh) & 0xffffu;
+        const uint32_t k1 = (w[1][e >> 1] >> sh) & 0xffffu;
+        const uint32_t k2 = (w[2][e >> 1] >> sh) & 0xffffu;
+        const uint32_t k3 = (w[3][e >> 1] >> sh) & 0xffffu;
+        uint2 v;
+        v.x = k0 | (k1 << 16);
+        v.y = k2 | (k3 << 16);
+        *reinterpret_cast<uint2 *>(&sm.vt[(vdg * 8 + e) * VS + pos]) = v;
+      }
+    }
+  };
+
+  f32x16_t o[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) o[db][x] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+
+  if (ntiles > 0) fetch(0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    __syncthreads();  // every wave is done reading the previous tile
+    stash();
+    __syncthreads();
+    if (tile + 1 < ntiles) fetch(tile + 1);
+
+    // S^T for the two 32-key blocks of the tile.
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) sacc[kb][x] = 0.f;
+      const uint16_t *krow = &sm.k[(kb * 32 + col) * KS + 8 * half];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const uint4 kf = *reinterpret_cast<const uint4 *>(krow + 16 * s);
+        sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+      }
+    }
+
+    // Scale to base 2, mask, online softmax over this lane's row.
+    const int kbase_idx = tile * BN;
+    const bool need_mask = kbase_idx + BN > wave_min_lim;
+    float tmax = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        float v = sacc[kb][x] * a.scale_log2;
+        if (need_mask) {
+          const int key = kbase_idx + kb * 32 + 8 * (x >> 2) + 4 * half + (x & 3);
+          if (key >= lim) v = kNegInf;
+        }
+        sacc[kb][x] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float mref = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - mref);
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const float p = fast_exp2(sacc[kb][x] - mref);
+        sacc[kb][x] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) o[db][x] *= alpha;
+
+    // O^T += V^T P^T over the four 16-key steps of the tile.
+#pragma unroll
+    for (int ts = 0; ts < 4; ++ts) {
+      const int kb = ts >> 1;
+      const int x0 = 8 * (ts & 1);
+      uint4 pf;
+      pf.x = pack_bf16x2(sacc[kb][x0 + 0], sacc[kb][x0 + 1]);
+      pf.y = pack_bf16x2(sacc[kb][x0 + 2], sacc[kb][x0 + 3]);
+      pf.z = pack_bf16x2(sacc[kb][x0 + 4], sacc[kb][x0 + 5]);
+      pf.w = pack_bf16x2(sacc[kb][x0 + 6], sacc[kb][x0 + 7]);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const uint4 vf =
+            *reinterpret_cast<const uint4 *>(&sm.vt[(db * 32 + col) * VS + 16 * ts + 8 * half]);
+        o[db] = mfma32(vf, pf, o[db]);
+      }
+    }
+  }
+
+  if (!row_ok) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((int64_t)(q0 + t) * a.n_heads + h) * D;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int x4 = 0; x4 < 4; ++x4) {
+      const int d0 = db * 32 + 8 * x4 + 4 * half;
+      uint2 w;
+      w.x = pack_bf16x2(o[db][4 * x4 + 0] * inv, o[db][4 * x4 + 1] * inv);
+      w.y = pack_bf16x2(o[db][4 * x4 + 2] * inv, o[db][4 * x4 + 3] * inv);
+      *reinterpret_cast<uint2 *>(orow + d0) = w;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, hipStream_t stream) {
+  const int64_t row_blocks = ((int64_t)a.max_q_len * a.group + BM - 1) / BM;
+  if (row_blocks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((uint32_t)row_blocks, a.n_kv_heads, a.batch);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, stream, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pkv
