@@ -1,0 +1,468 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the decode path over one batch: the K/V write of the
+step's new token (kv_store), the split-KV paged decode and the merge.  The
+headline workload is the Llama-3-8B-shaped single-request decode at the
+longest sweep context (32 query / 8 kv heads, head_dim 128, bf16, 65536-slot
+pool, 32 layers, seq_len 32768).  Successive steps attend successive layers
+(31, 30, ..., 0, 31, ...) of the 32-layer pool, as a model forward does, so
+each step's K/V come from HBM rather than from the 256 MB last-level cache.
+The K timed steps are replayed from one captured HIP graph.
+
+Printed as ONE JSON line (rank 0): value = algorithmic bytes per step /
+time per step (GB/s).  Extra fields: the B=1 decode latency sweep
+(1K..32K), the ragged causal prefill (TFLOP/s), the batched prefix-sharing
+and long-context decodes (GB/s), the roofline of the dominant kernel
+(paged_decode's split kernel, timed per launch with HIP events on its
+stream), and the CPU fp64 oracle's throughput on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 matrix
+METRIC = "paged decode achieved HBM GB/s (% peak) + prefill TFLOP/s; B=1 decode µs @1K–32K"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# launch plumbing: prebuilt ctypes arguments, direct calls into libpkv
+# ---------------------------------------------------------------------------
+class DecodeRunner:
+    """One decode workload on the device with its C-ABI arguments prebuilt."""
+
+    def __init__(self, case, fill_all_layers=True, num_splits=None):
+        import torch
+        import workloads as W
+        from paged_kv_attention_12_amd import api, binding as B
+        self.torch = torch
+        self.case = case
+        self.lib = B.load()
+        t = W.make_tensors(case, device="cuda", poison=not fill_all_layers)
+        if fill_all_layers and case.n_layers > 1:
+            g = torch.Generator(device="cuda")
+            g.manual_seed(case.seed + 99)
+            for layer in range(case.n_layers):
+                if layer != case.layer_id:
+                    W._fill_normal(t["k_buffer"][layer], g, case.k_scale)
+                    W._fill_normal(t["v_buffer"][layer], g)
+        self.t = t
+        self.step = api.DeviceStep(case.req_pool_indices, case.seq_lens, case.req_to_token)
+        H, d = case.n_heads, case.head_dim
+        self.num_splits = num_splits or B.pkv_decode_pick_splits(
+            case.batch, case.n_kv_heads, H, self.step.max_len, self.step.total_len)
+        self.ws = api.decode_workspace(case.batch, H, d, self.num_splits)
+        self.ws_bytes = self.ws.numel() * 4
+        self.out = torch.empty_like(t["q"])
+        self.pool = B.make_pool(t["k_buffer"], t["v_buffer"], t["req_to_token"])
+        self.pool_ref = C.byref(self.pool)
+        self.step_ref = C.byref(self.step.c)
+        self.out_dtype = B.dtype_code(self.out)
+        self.scale = case.sm_scale
+        self.ptr = {k: t[k].data_ptr() for k in ("q", "k_new", "v_new")}
+        self.loc = self.step.out_cache_loc.data_ptr()
+
+    def stream(self):
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def store(self, layer, st):
+        r = self.lib.pkv_kv_store(self.pool_ref, layer, self.ptr["k_new"], self.ptr["v_new"],
+                                  self.loc, self.step.n_new, st)
+        assert r == 0, r
+
+    def decode(self, layer, st):
+        r = self.lib.pkv_paged_decode(self.pool_ref, layer, self.step_ref, self.ptr["q"],
+                                      self.case.n_heads, self.scale, self.num_splits,
+                                      self.ws.data_ptr(), self.ws_bytes, st)
+        assert r == 0, r
+
+    def merge(self, st):
+        r = self.lib.pkv_paged_decode_merge(self.case.batch, self.case.n_heads,
+                                            self.case.head_dim, self.out_dtype, self.num_splits,
+                                            self.ws.data_ptr(), self.ws_bytes,
+                                            self.out.data_ptr(), st)
+        assert r == 0, r
+
+    def run_step(self, layer):
+        st = self.stream()
+        self.store(layer, st)
+        self.decode(layer, st)
+        self.merge(st)
+
+    def layer_of(self, k):
+        n = self.case.n_layers
+        return (self.case.layer_id - k) % n
+
+    # ---- algorithmic work ----
+    def kernel_bytes(self):
+        """Split kernel per launch: every key/value row of every request once,
+        the slot ids, and q."""
+        c = self.case
+        row = c.n_kv_heads * c.head_dim * 2
+        L = int(c.seq_lens.sum())
+        return L * 2 * row + L * 4 + c.batch * c.n_heads * c.head_dim * 2
+
+    def unique_kernel_bytes(self):
+        c = self.case
+        row = c.n_kv_heads * c.head_dim * 2
+        uniq = len(c.referenced_slots())
+        return uniq * 2 * row + int(c.seq_lens.sum()) * 4 + c.batch * c.n_heads * c.head_dim * 2
+
+    def step_bytes(self):
+        """kv_store (new rows read + written) + split kernel + merged output."""
+        c = self.case
+        row = c.n_kv_heads * c.head_dim * 2
+        return self.kernel_bytes() + 4 * c.batch * row + c.batch * c.n_heads * c.head_dim * 2
+
+
+def graph_steps(runner, n, start=0):
+    """Capture n consecutive steps (layer rotation from step `start`) in one graph."""
+    torch = runner.torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        runner.run_step(runner.layer_of(start))  # touch everything once outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for k in range(start, start + n):
+            runner.run_step(runner.layer_of(k))
+    torch.cuda.synchronize()
+    return g
+
+
+def timed_graph(runner, steps, warmup):
+    """W warm-up steps, then exactly K steps replayed from one graph, with a
+    device synchronize on both sides of the timed replay."""
+    torch = runner.torch
+    gw = graph_steps(runner, max(1, warmup))
+    gk = graph_steps(runner, steps, start=max(1, warmup))
+    gw.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gk.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    # the graph's result equals an eager run of the same last step
+    ref = runner.out.clone()
+    runner.run_step(runner.layer_of(max(1, warmup) + steps - 1))
+    torch.cuda.synchronize()
+    graph_ok = bool(torch.equal(ref, runner.out))
+    del gw, gk
+    return dt / steps, graph_ok
+
+
+def kernel_event_times(runner, launches, reps=3):
+    """Average duration of the split kernel: HIP events on its stream bracket
+    the replay of a graph holding `launches` back-to-back split-kernel
+    launches (successive layers); returns one average per replay."""
+    torch = runner.torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        runner.run_step(runner.layer_of(0))
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        st = runner.stream()
+        for k in range(launches):
+            runner.decode(runner.layer_of(k), st)
+    torch.cuda.synchronize()
+    g.replay()  # warm
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    out = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        g.replay()
+        b.record(cur)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) * 1e-3 / launches)
+    del g
+    return np.array(out)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def prefill_flops(case):
+    d, H = case.head_dim, case.n_heads
+    tot = 0
+    for L, q in zip(case.seq_lens.astype(np.int64), case.q_lens.astype(np.int64)):
+        p = L - q
+        tot += q * p + q * (q + 1) // 2
+    return 4 * d * H * int(tot)
+
+
+def bench_prefill(reps=20):
+    import torch
+    import workloads as W
+    from paged_kv_attention_12_amd import api, binding as B
+    case = W.ragged_prefill()
+    t = W.make_tensors(case, device="cuda", poison=False)
+    step = api.DeviceStep(case.req_pool_indices, case.seq_lens, case.req_to_token, case.q_lens)
+    out = torch.empty_like(t["q"])
+    lib = B.load()
+    pool = B.make_pool(t["k_buffer"], t["v_buffer"], t["req_to_token"])
+    st = torch.cuda.current_stream().cuda_stream
+    cur = torch.cuda.current_stream()
+
+    def store():
+        assert lib.pkv_kv_store(C.byref(pool), 0, t["k_new"].data_ptr(), t["v_new"].data_ptr(),
+                                step.out_cache_loc.data_ptr(), step.n_new, st) == 0
+
+    def attend():
+        assert lib.pkv_paged_prefill(C.byref(pool), 0, C.byref(step.c), t["q"].data_ptr(),
+                                     case.n_heads, case.sm_scale, 1, out.data_ptr(), st) == 0
+
+    for _ in range(3):
+        store()
+        attend()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b, c in ev:
+        a.record(cur)
+        store()
+        b.record(cur)
+        attend()
+        c.record(cur)
+    torch.cuda.synchronize()
+    t_store = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e-3
+    t_pre = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e-3
+    flops = prefill_flops(case)
+    med = float(np.median(t_pre))
+    row = case.n_kv_heads * case.head_dim * 2
+    return {
+        "workload": "ragged_causal_prefill_16req",
+        "n_new_tokens": int(case.q_lens.sum()), "kv_tokens": int(case.seq_lens.sum()),
+        "flops": flops, "prefill_ms": med * 1e3, "prefill_ms_p10_p90":
+            [float(np.percentile(t_pre, 10)) * 1e3, float(np.percentile(t_pre, 90)) * 1e3],
+        "tflops": flops / med / 1e12, "frac_of_bf16_peak": flops / med / 1e12 / BF16_PEAK_TFLOPS,
+        "kv_store_ms": float(np.median(t_store)) * 1e3,
+        "kv_store_gbps": 4 * step.n_new * row / float(np.median(t_store)) / 1e9,
+    }
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the headline workload)
+# ---------------------------------------------------------------------------
+def cpu_baseline(runner, budget_s=15.0):
+    import oracle
+    import torch
+    case = runner.case
+    layer = case.layer_id
+    slots = case.referenced_slots()
+    idx = torch.from_numpy(slots).cuda()
+    k = runner.t["k_buffer"][layer].index_select(0, idx).float().cpu().numpy()[None]
+    v = runner.t["v_buffer"][layer].index_select(0, idx).float().cpu().numpy()[None]
+    table = np.zeros_like(case.req_to_token)
+    for b in range(case.batch):
+        r = int(case.req_pool_indices[b])
+        L = int(case.seq_lens[b])
+        table[r, :L] = np.searchsorted(slots, case.req_to_token[r, :L])
+    q = runner.t["q"].float().cpu().numpy()
+    kn = runner.t["k_new"].float().cpu().numpy()
+    vn = runner.t["v_new"].float().cpu().numpy()
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        md = oracle.build_step(case.req_pool_indices, case.seq_lens, table)
+        k2, v2 = oracle.kv_store(k, v, 0, md["out_cache_loc"], kn, vn)
+        oracle.decode(k2, v2, 0, table, case.req_pool_indices, case.seq_lens, q, case.sm_scale)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or n >= 200:
+            break
+    per = dt / n
+    return {"value": runner.step_bytes() / per / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} full decode steps of {case.name} (kv_store + attention of all "
+                      f"{case.n_heads} heads over {int(case.seq_lens[0])} keys), numpy fp64, "
+                      f"{per * 1e3:.1f} ms/step"}
+
+
+# ---------------------------------------------------------------------------
+def counters_for(kernel_src_hash):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "decode_split_mfma_llama_b1_L32768.counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("source_sha256") != kernel_src_hash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def src_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "device.hpp"):
+        h.update(open(os.path.join(ROOT, "paged_kv_attention_12_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="skip the sweep, prefill and the other decode workloads")
+    ap.add_argument("--kernel-launches", type=int, default=64)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+            "(the path is single-GPU; see the sharding design notes)")
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        log("bench.py runs as a single process on one GPU")
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    from paged_kv_attention_12_amd import binding as B
+    B.load()
+
+    if args.copy_calibration:
+        # A plain copy of known size: its HBM counters give the scale between
+        # counter units and bytes on this machine.
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies (read 1 GiB + write 1 GiB each)")
+        del src, dst
+
+    # ---- headline: Llama-3-8B-shaped B=1 decode, seq_len 32768 ----
+    L_head = W.LLAMA_SWEEP[-1]
+    log(f"headline: llama B=1 decode L={L_head}")
+    head = DecodeRunner(W.llama_b1_decode(L_head))
+    sec_per_step, graph_ok = timed_graph(head, args.steps, args.warmup)
+    step_bytes = head.step_bytes()
+    value = step_bytes / sec_per_step / 1e9
+    kt = kernel_event_times(head, args.kernel_launches)
+    k_avg = float(kt.mean())
+    k_bytes = head.kernel_bytes()
+    achieved = k_bytes / k_avg / 1e9
+    traffic = counters_for(src_hash())
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                "kernel": "decode_split_mfma_kernel", "bytes_per_launch": k_bytes,
+                "avg_launch_us": k_avg * 1e6, "launches": int(len(kt)) * args.kernel_launches,
+                "timing": "HIP events around a graph of back-to-back split-kernel launches",
+                "num_splits": head.num_splits}
+    log(f"  step {sec_per_step * 1e6:.1f} us  {value:.0f} GB/s; split kernel {k_avg * 1e6:.1f} us "
+        f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBPS:.1%})  graph_ok={graph_ok}")
+
+    extra = {}
+    if not args.only_headline:
+        sweep = {}
+        for L in W.LLAMA_SWEEP:
+            r = head if L == L_head else DecodeRunner(W.llama_b1_decode(L))
+            spp, ok = timed_graph(r, 50, 5)
+            kt_l = kernel_event_times(r, 32, reps=2)
+            sweep[str(L)] = {"step_us": spp * 1e6, "split_kernel_us": float(kt_l.mean()) * 1e6,
+                             "step_gbps": r.step_bytes() / spp / 1e9,
+                             "split_kernel_gbps": r.kernel_bytes() / float(kt_l.mean()) / 1e9,
+                             "num_splits": r.num_splits, "graph_ok": ok}
+            log(f"  B=1 L={L}: step {spp * 1e6:.1f} us, split kernel {kt_l.mean() * 1e6:.1f} us")
+            if r is not head:
+                del r
+                torch.cuda.empty_cache()
+        extra["b1_decode_us"] = {L: v["step_us"] for L, v in sweep.items()}
+        extra["b1_decode_sweep"] = sweep
+
+        log("batched prefix-sharing decode")
+        rb = DecodeRunner(W.batched_prefix_decode())
+        spp, ok = timed_graph(rb, 20, 3)
+        ktb = kernel_event_times(rb, 8, reps=2)
+        extra["batched_prefix_decode"] = {
+            "step_us": spp * 1e6, "split_kernel_us": float(ktb.mean()) * 1e6,
+            "gbps_unique": rb.unique_kernel_bytes() / float(ktb.mean()) / 1e9,
+            "gbps_logical": rb.kernel_bytes() / float(ktb.mean()) / 1e9,
+            "num_splits": rb.num_splits, "graph_ok": ok}
+        del rb
+        torch.cuda.empty_cache()
+
+        log("long-context decode")
+        rl = DecodeRunner(W.long_context_decode())
+        spp, ok = timed_graph(rl, 10, 2)
+        ktl = kernel_event_times(rl, 4, reps=2)
+        extra["long_context_decode"] = {
+            "step_us": spp * 1e6, "split_kernel_us": float(ktl.mean()) * 1e6,
+            "gbps": rl.kernel_bytes() / float(ktl.mean()) / 1e9,
+            "frac_of_hbm_peak": rl.kernel_bytes() / float(ktl.mean()) / 1e9 / HBM_PEAK_GBPS,
+            "num_splits": rl.num_splits, "graph_ok": ok}
+        del rl
+        torch.cuda.empty_cache()
+
+        log("ragged prefill")
+        extra["prefill"] = bench_prefill()
+        log(f"  prefill {extra['prefill']['prefill_ms']:.3f} ms "
+            f"{extra['prefill']['tflops']:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu oracle baseline")
+        cpu = cpu_baseline(head)
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": sec_per_step * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"llama3_8b_shape_b1_decode_L{L_head}", "batch": 1,
+                   "n_heads": 32, "n_kv_heads": 8, "head_dim": 128, "seq_len": L_head,
+                   "pool_slots": 65536, "n_layers": 32, "step": "kv_store+paged_decode+merge",
+                   "layer_rotation": "31,30,...,0", "timing": "one HIP graph of K steps",
+                   "num_splits": head.num_splits, "bytes_per_step": step_bytes},
+        "hbm_frac": value / HBM_PEAK_GBPS,
+        "graph_replay_matches_eager": graph_ok,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    rec.update(extra)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

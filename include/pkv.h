@@ -159,11 +159,14 @@ pkv_status pkv_kv_store(const pkv_pool *pool, int32_t layer_id, const void *k_ne
 size_t pkv_decode_workspace_bytes(int32_t max_batch, int32_t n_heads, int32_t head_dim,
                                   int32_t num_splits);
 
-/* Host-only split-count heuristic (no device access, no sync): picks the
- * number of KV splits for a decode launch from batch, n_kv_heads and the host
- * max_len so that the launch fills the device, capped at max_splits (>= 1). */
+/* Host-only split-count heuristic (no device access, no sync).  From the
+ * batch, head counts, the host max_len and the step's total context tokens
+ * (kv_indptr[batch]; <= 0 means batch * max_len) it picks num_splits for
+ * pkv_paged_decode: for equal lengths about one long-running wavefront per
+ * SIMD, for ragged lengths many short splits (at most 256 tokens) so the
+ * device balances the load; clamped to [1, max_splits]. */
 int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_heads,
-                               int32_t max_len, int32_t max_splits);
+                               int32_t max_len, int64_t total_len, int32_t max_splits);
 
 /* ------------------------------------------------------------------------
  * Split-KV paged decode ("Inference" guide, section "KV Cache": the single

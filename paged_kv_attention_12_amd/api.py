@@ -25,6 +25,7 @@ class DeviceStep:
         self.n_new = md["n_new"]
         self.max_len = md["max_len"]
         self.max_q_len = md["max_q_len"]
+        self.total_len = int(md["kv_indptr"][-1])
         self.decode = q_lens is None
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
         self.req_pool_indices = to(B._host_i32(req_pool_indices, "req_pool_indices"))
@@ -53,7 +54,7 @@ def decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceSte
     H, d = int(q.shape[1]), int(q.shape[2])
     if num_splits is None:
         num_splits = B.pkv_decode_pick_splits(step.batch, int(k_buffer.shape[2]), H,
-                                              step.max_len)
+                                              step.max_len, step.total_len)
     if workspace is None:
         workspace = decode_workspace(step.batch, H, d, num_splits, q.device)
     if out is None:

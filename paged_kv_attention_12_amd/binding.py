@@ -74,6 +74,10 @@ def load() -> C.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"libpkv.so not built at {_LIB_PATH}; run "
                           "`python -m paged_kv_attention_12_amd.build`")
+    try:  # let torch bring its HIP runtime in first, so both share one runtime
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = C.CDLL(_LIB_PATH)
     P = C.c_void_p
     i32, i64, f32, sz = C.c_int32, C.c_int64, C.c_float, C.c_size_t
@@ -84,7 +88,7 @@ def load() -> C.CDLL:
         "pkv_validate_step": (C.c_int, [i64, i64, i64, P, i32, P, P, P, P, P, i64]),
         "pkv_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, P, i64, P]),
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
-        "pkv_decode_pick_splits": (i32, [i32, i32, i32, i32, i32]),
+        "pkv_decode_pick_splits": (i32, [i32, i32, i32, i32, i64, i32]),
         "pkv_paged_decode": (C.c_int, [C.POINTER(pkv_pool), i32, C.POINTER(pkv_step), P, i32,
                                        f32, i32, P, sz, P]),
         "pkv_paged_decode_merge": (C.c_int, [i32, i32, i32, C.c_int, i32, P, sz, P, P]),
@@ -261,8 +265,9 @@ def pkv_decode_workspace_bytes(max_batch: int, n_heads: int, head_dim: int,
 
 
 def pkv_decode_pick_splits(batch: int, n_kv_heads: int, n_heads: int, max_len: int,
-                           max_splits: int = 1024) -> int:
-    return int(load().pkv_decode_pick_splits(batch, n_kv_heads, n_heads, max_len, max_splits))
+                           total_len: int = 0, max_splits: int = 1024) -> int:
+    return int(load().pkv_decode_pick_splits(batch, n_kv_heads, n_heads, max_len,
+                                             int(total_len), max_splits))
 
 
 def pkv_paged_decode(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,

@@ -58,6 +58,9 @@ __device__ __forceinline__ float slice_dot(const uint4 &q, const uint4 &k) {
   }
 }
 
+// Slot ids of one split are staged in LDS in rounds of this many tokens.
+constexpr int kSlotTile = 2048;
+
 template <typename T, int D, int NG, int U>
 __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
   constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane per row
@@ -65,31 +68,33 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
   constexpr int TPW = 64 / LPT;             // rows per wave per load
   constexpr int STEP = TPW * U;             // tokens per iteration
   static_assert(LPT >= 4 && LPT <= 64 && 64 % LPT == 0, "row width");
+  __shared__ int32_t s_slot[kSlotTile];
+
+  const int b = blockIdx.z;
+  const int s = blockIdx.y;
+  const int L = a.seq_lens[b];
+  const int start = s * a.chunk;
+  const int end = min(L, start + a.chunk);
 
   const int lane = threadIdx.x & 63;
   const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= a.n_kv_heads * a.n_chunks) return;
-  const int b = blockIdx.z;
-  const int s = blockIdx.y;
-  const int hk = task / a.n_chunks;
-  const int g0 = (task - hk * a.n_chunks) * a.heads_per_chunk;
-  const int ng = min(a.heads_per_chunk, a.group - g0);
+  // Waves past the last task still take part in the workgroup barriers.
+  const bool active = task < a.n_kv_heads * a.n_chunks;
+  const int hk = active ? task / a.n_chunks : 0;
+  const int g0 = active ? (task - hk * a.n_chunks) * a.heads_per_chunk : 0;
+  const int ng = active ? min(a.heads_per_chunk, a.group - g0) : 0;
   const int h0 = hk * a.group + g0;
   const int row = lane / LPT;
   const int part = lane - row * LPT;
   const int S = a.num_splits;
-
-  const int L = a.seq_lens[b];
-  const int start = s * a.chunk;
-  const int end = min(L, start + a.chunk);
   const int64_t p0 = ((int64_t)b * a.n_heads + h0) * S + s;  // partial row of head h0
 
-  if (start >= end) {  // empty split: (m, l) = (-inf, 0), o = 0
-    if (row == 0) {
+  if (start >= end) {  // empty split (uniform over the workgroup): (-inf, 0), o = 0
+    if (active && row == 0) {
       for (int g = 0; g < ng; ++g) {
-        float *o = a.o_part + (p0 + (int64_t)g * S) * D + part * EPL;
+        float4 *o = reinterpret_cast<float4 *>(a.o_part + (p0 + (int64_t)g * S) * D + part * EPL);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+        for (int e = 0; e < EPL; e += 4) o[e / 4] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (part == 0) {
           a.ml_part[(p0 + (int64_t)g * S) * 2 + 0] = kNegInf;
           a.ml_part[(p0 + (int64_t)g * S) * 2 + 1] = 0.f;
@@ -122,37 +127,35 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
     for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
-  for (int j0 = start; j0 < end; j0 += STEP) {
-    int slot[U];
-    bool ok[U];
+  // Gather the rows of tokens j0 + u * TPW + row (u < U) of the current round.
+  auto fetch = [&](uint4(&kx)[U], uint4(&vx)[U], int j0, int r0, int r1) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * TPW + row;
-      ok[u] = j < end;
-      slot[u] = ok[u] ? table[j] : 0;
-    }
-    uint4 kx[U], vx[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
       kx[u] = make_uint4(0u, 0u, 0u, 0u);
       vx[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (ok[u]) {
-        kx[u] = load16(kbase + (int64_t)slot[u] * row_elems);
-        vx[u] = load16(vbase + (int64_t)slot[u] * row_elems);
+      if (j < r1) {
+        const int64_t off = (int64_t)s_slot[j - r0] * row_elems;
+        kx[u] = load16(kbase + off);
+        vx[u] = load16(vbase + off);
       }
     }
+  };
+
+  // Scores, then the online-softmax update of this row group's state.
+  auto process = [&](const uint4(&kx)[U], const uint4(&vx)[U], int j0, int r1) {
     float sc[U][NG];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int g = 0; g < NG; ++g) sc[u][g] = group_sum<LPT>(slice_dot<T>(qv[g], kx[u]));
-
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       float mt = kNegInf;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        sc[u][g] = ok[u] ? sc[u][g] * a.scale_log2 : kNegInf;
+        const bool ok = j0 + u * TPW + row < r1;
+        sc[u][g] = ok ? sc[u][g] * a.scale_log2 : kNegInf;
         mt = fmaxf(mt, sc[u][g]);
       }
       const float mn = fmaxf(m[g], mt);
@@ -170,7 +173,32 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
       }
       m[g] = mn;
     }
+  };
+
+  uint4 ka[U], va[U], kb[U], vb[U];
+  for (int r0 = start; r0 < end; r0 += kSlotTile) {
+    const int r1 = min(end, r0 + kSlotTile);
+    if (r0 != start) __syncthreads();  // every wave is done with the previous round
+    for (int j = r0 + (int)threadIdx.x; j < r1; j += 256) s_slot[j - r0] = table[j];
+    __syncthreads();
+    if (!active) continue;
+    // Two register sets: the rows of the next iteration are in flight while
+    // the current ones are used.
+    int j0 = r0;
+    fetch(ka, va, j0, r0, r1);
+    while (true) {
+      const int j1 = j0 + STEP;
+      if (j1 < r1) fetch(kb, vb, j1, r0, r1);
+      process(ka, va, j0, r1);
+      if (j1 >= r1) break;
+      const int j2 = j1 + STEP;
+      if (j2 < r1) fetch(ka, va, j2, r0, r1);
+      process(kb, vb, j1, r1);
+      if (j2 >= r1) break;
+      j0 = j2;
+    }
   }
+  if (!active) return;
 
   // Combine the TPW row states of the wave (rows sit LPT lanes apart).
 #pragma unroll
@@ -210,42 +238,291 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
   }
 }
 
-// One group of D/4 threads per (request, head) row; 4 consecutive dims each.
+// One workgroup per (request, head) row.  The splits are spread over
+// 256 / (D/4) split groups of D/4 threads (4 dims each) so that many partial
+// loads are in flight; the groups' sums are then added through LDS.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(const MergeArgs a) {
   constexpr int TPR = D / 4;
-  constexpr int RPB = 256 / TPR;
-  const int r = blockIdx.x * RPB + threadIdx.x / TPR;
-  const int c = threadIdx.x % TPR;
-  if (r >= a.rows) return;
+  constexpr int SG = 256 / TPR;
+  __shared__ float s_red[8];
+  __shared__ float4 s_num[SG][TPR];
+  __shared__ float s_den[SG];
+  const int r = blockIdx.x;
+  const int t = threadIdx.x;
   const int S = a.num_splits;
   const float *ml = a.ml_part + (int64_t)r * S * 2;
-  const float *op = a.o_part + (int64_t)r * S * D + c * 4;
+  const float *op = a.o_part + (int64_t)r * S * D;
+
+  // M = max over non-empty splits
   float M = kNegInf;
-  for (int s = 0; s < S; ++s)
+  for (int s = t; s < S; s += 256)
     if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
-  float den = 0.f, n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ls = ml[2 * s + 1];
-    if (ls > 0.f) {
-      const float w = ls * fast_exp2(ml[2 * s] - M);
-      const float4 o = *reinterpret_cast<const float4 *>(op + (int64_t)s * D);
-      den += w;
-      n0 = fmaf(w, o.x, n0);
-      n1 = fmaf(w, o.y, n1);
-      n2 = fmaf(w, o.z, n2);
-      n3 = fmaf(w, o.w, n3);
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+  if ((t & 63) == 0) s_red[t >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float Mr = (M == kNegInf) ? 0.f : M;
+
+  const int sg = t / TPR;
+  const int c = t - sg * TPR;
+  float den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  // KB splits per thread per batch: all their loads are issued before any is
+  // used, so a batch costs one memory round trip.
+  constexpr int KB = 16;
+  for (int s0 = sg; s0 < S; s0 += SG * KB) {
+    float4 ov[KB];
+    float mv[KB], lv[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int s = min(s0 + SG * k, S - 1);
+      ov[k] = *reinterpret_cast<const float4 *>(op + (int64_t)s * D + c * 4);
+      mv[k] = ml[2 * s];
+      lv[k] = (s0 + SG * k < S) ? ml[2 * s + 1] : 0.f;
     }
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const float w = lv[k] > 0.f ? lv[k] * fast_exp2(mv[k] - Mr) : 0.f;
+      den += w;
+      num.x = fmaf(w, ov[k].x, num.x);
+      num.y = fmaf(w, ov[k].y, num.y);
+      num.z = fmaf(w, ov[k].z, num.z);
+      num.w = fmaf(w, ov[k].w, num.w);
+    }
+  }
+  s_num[sg][c] = num;
+  if (c == 0) s_den[sg] = den;
+  __syncthreads();
+  if (sg != 0) return;
+  den = 0.f;
+  num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int g = 0; g < SG; ++g) {
+    const float4 o = s_num[g][c];
+    num.x += o.x;
+    num.y += o.y;
+    num.z += o.z;
+    num.w += o.w;
+    den += s_den[g];
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   if constexpr (sizeof(T) == 2) {
     uint2 w;
-    w.x = pack_bf16x2(n0 * inv, n1 * inv);
-    w.y = pack_bf16x2(n2 * inv, n3 * inv);
+    w.x = pack_bf16x2(num.x * inv, num.y * inv);
+    w.y = pack_bf16x2(num.z * inv, num.w * inv);
     *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + (int64_t)r * D + c * 4) = w;
   } else {
     *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + (int64_t)r * D + c * 4) =
-        make_float4(n0 * inv, n1 * inv, n2 * inv, n3 * inv);
+        make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16, head_dim 128: the same split decode with both contractions on
+// v_mfma_f32_16x16x32_bf16.  A wavefront owns (request, split, kv-head, up to
+// 16 query heads of its group; unused columns are zero).  Per iteration it
+// takes 32 keys:
+//   S^T (keys x heads) = K Q^T   A = K rows, loaded straight from the pool in
+//                                operand layout (lane c%16 <-> key, lane
+//                                group <-> 8 dims), B = Q held in registers;
+//   O^T (dims x heads) += V^T P^T  A = V^T, built in registers from V rows
+//                                loaded whole (lane c <-> 8 dims, lane group
+//                                g <-> 8 keys) by an 8 x 8 bf16 transpose,
+//                                B = P^T taken from the S^T accumulators.
+// Lane (c, g) = (lane % 16, lane / 16) holds S^T for keys 16t + 4g + i
+// (tile t, i < 4) of head c, so a head's running max is shared across the four
+// lane groups with two xor shuffles; the running sums stay per lane until the
+// end.  Rows of the next iteration are in flight while the current ones are
+// used.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, const f32x4_t &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs a) {
+  constexpr int P = 2;  // register tile sets (deeper rings measured no faster)
+  constexpr int D = 128;
+  constexpr int KT = 32;  // keys per iteration
+  __shared__ int32_t s_slot[kSlotTile];
+
+  const int b = blockIdx.z;
+  const int s = blockIdx.y;
+  const int L = a.seq_lens[b];
+  const int start = s * a.chunk;
+  const int end = min(L, start + a.chunk);
+
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const bool active = task < a.n_kv_heads * a.n_chunks;
+  const int hk = active ? task / a.n_chunks : 0;
+  const int g0 = active ? (task - hk * a.n_chunks) * a.heads_per_chunk : 0;
+  const int ng = active ? min(a.heads_per_chunk, a.group - g0) : 0;
+  const int h0 = hk * a.group + g0;
+  const bool col_ok = c < ng;
+  const int S = a.num_splits;
+  const int64_t pr = ((int64_t)b * a.n_heads + h0 + c) * S + s;  // partial row of head h0 + c
+
+  if (start >= end) {
+    if (active && col_ok) {
+      float4 *o = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) o[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (g == 0) {
+        a.ml_part[pr * 2 + 0] = kNegInf;
+        a.ml_part[pr * 2 + 1] = 0.f;
+      }
+    }
+    return;
+  }
+
+  // Q^T operand: head c, dims 8g + 32k .. +8 for step k.
+  uint4 qf[4];
+  {
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) +
+                           ((int64_t)b * a.n_heads + h0 + c) * D + 8 * g;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      qf[k] = (active && col_ok) ? load16(qrow + 32 * k) : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  const int32_t *table = a.req_to_token + (int64_t)a.req_pool_indices[b] * a.max_ctx_len;
+  const int64_t row_elems = (int64_t)a.n_kv_heads * D;
+  const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k_layer) + (int64_t)hk * D + 8 * g;
+  const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v_layer) + (int64_t)hk * D + 8 * c;
+
+  f32x4_t o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf;  // base-2 running max of head c (same in all four groups)
+  float l_lane = 0.f;     // this lane's share of the running sum
+
+  // K rows: keys 16t + c (t < 2), 16 bytes at dims 8g + 32k.  V rows: keys
+  // 4g + i and 16 + 4g + i (i < 4), dims 8c .. 8c + 7.  Tokens past the end
+  // of the round read the round's last row instead (finite data whose score is
+  // masked to -inf, so its weight is 0): the loads stay unconditional, which
+  // lets the compiler keep several tiles in flight.
+  auto fetch = [&](uint4(&kx)[2][4], uint4(&vx)[8], int j0, int r0, int r1) {
+    const int last = r1 - 1 - r0;
+    const int jb = j0 - r0;
+    int sk[2], sv[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sk[t] = s_slot[min(jb + 16 * t + c, last)];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) sv[x] = s_slot[min(jb + 16 * (x >> 2) + 4 * g + (x & 3), last)];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kx[t][k] = load16(kbase + (int64_t)sk[t] * row_elems + 32 * k);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) vx[x] = load16(vbase + (int64_t)sv[x] * row_elems);
+  };
+
+  auto process = [&](const uint4(&kx)[2][4], const uint4(&vx)[8], int j0, int r1) {
+    f32x4_t st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) st[t] = mfma16(kx[t][k], qf[k], st[t]);
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = j0 + 16 * t + 4 * g + i < r1;
+        st[t][i] = ok ? st[t][i] * a.scale_log2 : kNegInf;
+        mx = fmaxf(mx, st[t][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float mref = (m_new == kNegInf) ? 0.f : m_new;
+    if (__any(m_new != m_run)) {  // rescale only when some head's max moved
+      const float alpha = fast_exp2(m_run - mref);
+      l_lane *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] *= alpha;
+    }
+    m_run = m_new;
+    float p[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[4 * t + i] = fast_exp2(st[t][i] - mref);
+        l_lane += p[4 * t + i];
+      }
+    uint4 pf;
+    pf.x = pack_bf16x2(p[0], p[1]);
+    pf.y = pack_bf16x2(p[2], p[3]);
+    pf.z = pack_bf16x2(p[4], p[5]);
+    pf.w = pack_bf16x2(p[6], p[7]);
+    // V^T operand e: element x is dim 8c + e of key x's row.
+    const uint32_t w[8][4] = {
+        {vx[0].x, vx[0].y, vx[0].z, vx[0].w}, {vx[1].x, vx[1].y, vx[1].z, vx[1].w},
+        {vx[2].x, vx[2].y, vx[2].z, vx[2].w}, {vx[3].x, vx[3].y, vx[3].z, vx[3].w},
+        {vx[4].x, vx[4].y, vx[4].z, vx[4].w}, {vx[5].x, vx[5].y, vx[5].z, vx[5].w},
+        {vx[6].x, vx[6].y, vx[6].z, vx[6].w}, {vx[7].x, vx[7].y, vx[7].z, vx[7].w}};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t d[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t lo = w[2 * x][e >> 1], hi = w[2 * x + 1][e >> 1];
+        d[x] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      o[e] = mfma16(make_uint4(d[0], d[1], d[2], d[3]), pf, o[e]);
+    }
+  };
+
+  // Ring of P register tile sets: P - 1 tiles are in flight while one is used.
+  static_assert(P >= 2, "pipeline depth");
+  uint4 kr[P][2][4], vr[P][8];
+  for (int r0 = start; r0 < end; r0 += kSlotTile) {
+    const int r1 = min(end, r0 + kSlotTile);
+    if (r0 != start) __syncthreads();
+    for (int j = r0 + (int)threadIdx.x; j < r1; j += 256) s_slot[j - r0] = table[j];
+    __syncthreads();
+    if (!active) continue;
+    const int ntiles = (r1 - r0 + KT - 1) / KT;
+#pragma unroll
+    for (int q = 0; q < P - 1; ++q) fetch(kr[q], vr[q], r0 + q * KT, r0, r1);
+    int i = 0;
+    for (; i + P <= ntiles; i += P) {
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        fetch(kr[(q + P - 1) % P], vr[(q + P - 1) % P], r0 + (i + q + P - 1) * KT, r0, r1);
+        process(kr[q], vr[q], r0 + (i + q) * KT, r1);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < P - 1; ++q)
+      if (i + q < ntiles) process(kr[q], vr[q], r0 + (i + q) * KT, r1);
+  }
+  if (!active) return;
+
+  float l_tot = l_lane + __shfl_xor(l_lane, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (!col_ok) return;
+  // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
+  const float inv = 1.f / l_tot;
+  float4 *op = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    op[2 * i + 0] = make_float4(o[0][i] * inv, o[1][i] * inv, o[2][i] * inv, o[3][i] * inv);
+    op[2 * i + 1] = make_float4(o[4][i] * inv, o[5][i] * inv, o[6][i] * inv, o[7][i] * inv);
+  }
+  if (g == 0) {
+    a.ml_part[pr * 2 + 0] = m_run;
+    a.ml_part[pr * 2 + 1] = l_tot;
   }
 }
 
@@ -275,7 +552,20 @@ hipError_t decode_dispatch_ng(const DecodeArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream) {
+hipError_t launch_paged_decode(const DecodeArgs &args, int dtype, int head_dim,
+                               hipStream_t stream) {
+  DecodeArgs a = args;
+  // Query heads of a kv-head's group served by one wavefront: up to 16 on the
+  // matrix-core path (bf16, head_dim 128), up to 8 on the vector path.
+  const bool mfma = dtype == 1 && head_dim == 128;
+  const int per_wave = mfma ? 16 : 8;
+  a.n_chunks = (a.group + per_wave - 1) / per_wave;
+  a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
+  if (mfma) {
+    const dim3 grid((a.n_kv_heads * a.n_chunks + 3) / 4, a.num_splits, a.batch);
+    hipLaunchKernelGGL(decode_split_mfma_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   if (dtype == 1) {
     if (head_dim == 128) return decode_dispatch_ng<uint16_t, 128>(a, stream);
     if (head_dim == 64) return decode_dispatch_ng<uint16_t, 64>(a, stream);
@@ -287,9 +577,7 @@ hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hip
 }
 
 hipError_t launch_decode_merge(const MergeArgs &a, int dtype, int head_dim, hipStream_t stream) {
-  const int tpr = head_dim / 4;
-  const int rpb = 256 / tpr;
-  const dim3 grid((a.rows + rpb - 1) / rpb);
+  const dim3 grid(a.rows);
   if (dtype == 1) {
     if (head_dim == 128)
       hipLaunchKernelGGL((decode_merge_kernel<uint16_t, 128>), grid, dim3(256), 0, stream, a);

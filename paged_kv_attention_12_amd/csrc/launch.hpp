@@ -33,8 +33,8 @@ struct DecodeArgs {
   int32_t n_heads;
   int32_t n_kv_heads;
   int32_t group;              // n_heads / n_kv_heads
-  int32_t n_chunks;           // head chunks per kv-head (group split into chunks of <= 8)
-  int32_t heads_per_chunk;
+  int32_t n_chunks;           // head chunks per kv-head (set by the launcher)
+  int32_t heads_per_chunk;    // query heads per chunk (set by the launcher)
   int32_t num_splits;
   int32_t chunk;              // tokens per split (multiple of 16)
   float scale_log2;           // sm_scale * log2(e)

@@ -27,8 +27,6 @@ bool dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16; }
 
 // Token-range granularity of one split (rows per decode iteration divide it).
 constexpr int32_t kSplitAlign = 16;
-// Query heads one decode wavefront serves at most.
-constexpr int32_t kMaxHeadsPerWave = 8;
 
 pkv_status check_pool(const pkv_pool *p, int32_t layer_id) {
   if (!p || !p->k_buffer || !p->v_buffer || !p->req_to_token) return PKV_ERR_NULL;
@@ -175,18 +173,25 @@ size_t pkv_decode_workspace_bytes(int32_t max_batch, int32_t n_heads, int32_t he
 }
 
 int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_heads,
-                               int32_t max_len, int32_t max_splits) {
+                               int32_t max_len, int64_t total_len, int32_t max_splits) {
   if (batch <= 0 || n_kv_heads <= 0 || n_heads <= 0 || max_len <= 0) return 1;
   max_splits = std::max(1, max_splits);
+  if (total_len <= 0) total_len = (int64_t)batch * max_len;
   const int32_t group = std::max(1, n_heads / n_kv_heads);
-  const int32_t chunks = (group + kMaxHeadsPerWave - 1) / kMaxHeadsPerWave;
-  // Aim for about 4096 busy wavefronts (16 per CU on 256 CUs) while keeping
-  // at least 256 tokens per split so the per-split overhead stays small.
-  const int64_t waves_per_split = (int64_t)batch * n_kv_heads * chunks;
-  int64_t s = (4096 + waves_per_split - 1) / waves_per_split;
-  const int64_t by_len = std::max<int64_t>(1, ((int64_t)max_len + 255) / 256);
-  s = std::min(s, by_len);
+  // head chunks per kv-head on the matrix-core path (16 query heads per wave)
+  const int64_t chunks = (group + 15) / 16;
+  // Wavefront-tokens of work: every (kv-head, head chunk) walks every token.
+  const int64_t work = total_len * n_kv_heads * chunks;
+  // Equal lengths: about 1024 long-running wavefronts (one per SIMD) keep the
+  // per-split start-up and merge cost low.  Ragged lengths: short splits of at
+  // most 256 tokens, about 16K of them, so that the device balances the load.
+  const bool ragged = (int64_t)batch * max_len > total_len + total_len / 4;
+  int64_t chunk = ragged ? std::min<int64_t>(256, work / 16384)
+                         : std::min<int64_t>(2048, work / 1024);
+  chunk = std::max<int64_t>(chunk, 16);
+  int64_t s = ((int64_t)max_len + chunk - 1) / chunk;
   s = std::min<int64_t>(s, max_splits);
+  s = std::min<int64_t>(s, 65535);
   return (int32_t)std::max<int64_t>(1, s);
 }
 
@@ -207,7 +212,6 @@ pkv_status pkv_paged_decode(const pkv_pool *pool, int32_t layer_id, const pkv_st
   if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, pool->head_dim, num_splits))
     return PKV_ERR_WORKSPACE_TOO_SMALL;
   const int32_t group = n_heads / pool->n_kv_heads;
-  const int32_t chunks = (group + kMaxHeadsPerWave - 1) / kMaxHeadsPerWave;
   pkv::DecodeArgs a;
   a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
   a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
@@ -222,8 +226,8 @@ pkv_status pkv_paged_decode(const pkv_pool *pool, int32_t layer_id, const pkv_st
   a.n_heads = n_heads;
   a.n_kv_heads = pool->n_kv_heads;
   a.group = group;
-  a.n_chunks = chunks;
-  a.heads_per_chunk = (group + chunks - 1) / chunks;
+  a.n_chunks = 0;
+  a.heads_per_chunk = 0;
   a.num_splits = num_splits;
   a.chunk = decode_chunk(step->max_len, num_splits);
   a.scale_log2 = sm_scale * 1.4426950408889634f;

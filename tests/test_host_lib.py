@@ -129,8 +129,13 @@ def test_workspace_bytes_and_split_choice(lib):
                  (2, 2, 4, 17)]:
         s = B.pkv_decode_pick_splits(*args, max_splits=512)
         assert 1 <= s <= 512
-        assert s <= max(1, (args[3] + 255) // 256)
+        assert s <= max(1, (args[3] + 15) // 16)   # never below 16 tokens per split
     assert B.pkv_decode_pick_splits(1, 8, 32, 32768, max_splits=4) == 4
+    # the measured choices: B=1 Llama shapes, long context, ragged batch
+    assert B.pkv_decode_pick_splits(1, 8, 32, 32768, 32768) == 128
+    assert B.pkv_decode_pick_splits(1, 8, 32, 1024, 1024) == 64
+    assert B.pkv_decode_pick_splits(8, 8, 64, 131072, 8 * 131072) == 64
+    assert B.pkv_decode_pick_splits(64, 8, 32, 8192, 266000) == 64
 
 
 def _fake_pool(dtype=B.PKV_BF16, head_dim=128, n_layers=2):
