@@ -343,6 +343,8 @@ def main():
     ap.add_argument("--only-headline", action="store_true",
                     help="skip the sweep, prefill and the other decode workloads")
     ap.add_argument("--kernel-launches", type=int, default=64)
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the ragged prefill measurement and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (counter scale)")
     args = ap.parse_args()
@@ -360,6 +362,10 @@ def main():
     torch.cuda.set_device(0)
     from paged_kv_attention_12_amd import binding as B
     B.load()
+
+    if args.only_prefill:
+        print(json.dumps(bench_prefill()), flush=True)
+        return
 
     if args.copy_calibration:
         # A plain copy of known size: its HBM counters give the scale between

@@ -24,6 +24,8 @@
 // is being multiplied.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -66,8 +68,8 @@ template <int D>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
   constexpr int KS = Smem<D>::KS;
   constexpr int VS = Smem<D>::VS;
-  constexpr int KSTEPS = D / 16;      // MFMA steps over head_dim for S^T
-  constexpr int DBLK = D / 32;        // 32-dim blocks of O^T
+  constexpr int KSTEPS = D / 16;             // MFMA steps over head_dim for S^T
+  constexpr int DBLK = D / 32;               // 32-dim blocks of O^T
   constexpr int KPIECES = BN * D / 8 / 256;  // 16-byte K pieces per thread per tile
   constexpr int VJOBS = (BN / 4) * (D / 8);  // (4-key, 8-dim) V jobs per tile
   __shared__ Smem<D> sm;
@@ -99,15 +101,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
   // Keys visible to this row.
   const int lim = !row_ok ? 0 : (a.causal ? prefix + t + 1 : kv_len);
 
-  // Keys any row of the workgroup sees.
+  // Keys any row of the workgroup sees, and the tiles every row sees whole.
   const int r_last = min(rows, (rb + 1) * BM) - 1;
   const int kv_end = a.causal ? min(kv_len, prefix + r_last / G + 1) : kv_len;
   const int ntiles = (kv_end + BN - 1) / BN;
-  // Smallest per-row limit among this wave's valid rows: tiles wholly below it
-  // need no mask.
-  const int r_first = rb * BM + wave * WROWS;
-  const int wave_min_lim =
-      r_first >= rows ? 0 : (a.causal ? prefix + r_first / G + 1 : kv_len);
+  const int wg_min_lim = a.causal ? prefix + (rb * BM) / G + 1 : kv_len;
+  const int n_free = min(ntiles, wg_min_lim / BN);
 
   // Q (B operand of S^T): lane holds dims 16s + 8*half .. +8 of its row for step s.
   uint4 qf[KSTEPS];
@@ -124,32 +123,40 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
   const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k_layer) + (int64_t)hk * D;
   const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v_layer) + (int64_t)hk * D;
 
-  // Global -> register staging of one tile.
+  // Global -> register staging of one tile.  K: 16 lanes cover one key row.
+  // V: lanes first run over the 16 key quads of the tile, so that the
+  // transposed LDS writes of a 16-lane group fill 128 distinct bytes.
   uint4 kreg[KPIECES];
   uint4 vreg[4];
-  const int vjob = tid;  // V job: keys 4*(vjob / (D/8)) .. +3, dims 8*(vjob % (D/8)) .. +7
-  const int vkq = vjob / (D / 8);
-  const int vdg = vjob - vkq * (D / 8);
+  const int vkq = tid & 15;  // keys 4 * vkq .. + 3
+  const int vdg = tid >> 4;  // dims 8 * vdg .. + 7
+  const bool vjob = tid < VJOBS;
 
-  auto fetch = [&](int tile) {
+  // Slot ids are loaded one tile ahead of the rows they address, so a
+  // tile's K/V loads never wait on a table load.  Keys past kv_end read the
+  // last valid key instead (always masked), keeping every load unconditional.
+  int kslot[KPIECES], vslot[4];
+  auto load_slots = [&](int tile) {
     const int base = tile * BN;
 #pragma unroll
     for (int p = 0; p < KPIECES; ++p) {
-      const int piece = tid + 256 * p;
-      const int key = piece / (D / 8);
-      const int dg = piece - key * (D / 8);
-      const int j = base + key;
-      kreg[p] = make_uint4(0u, 0u, 0u, 0u);
-      if (j < kv_end) kreg[p] = load16(kbase + (int64_t)table[j] * row_elems + dg * 8);
+      const int key = (tid + 256 * p) / (D / 8);
+      kslot[p] = table[min(base + key, kv_end - 1)];
     }
-    if (vjob < VJOBS) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int j = base + vkq * 4 + c;
-        vreg[c] = make_uint4(0u, 0u, 0u, 0u);
-        if (j < kv_end) vreg[c] = load16(vbase + (int64_t)table[j] * row_elems + vdg * 8);
-      }
+    for (int c = 0; c < 4; ++c) vslot[c] = table[min(base + vkq * 4 + c, kv_end - 1)];
+  };
+  auto fetch = [&](int tile) {
+#pragma unroll
+    for (int p = 0; p < KPIECES; ++p) {
+      const int dg = (tid + 256 * p) % (D / 8);
+      kreg[p] = load16(kbase + (int64_t)kslot[p] * row_elems + dg * 8);
     }
+    if (vjob) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) vreg[c] = load16(vbase + (int64_t)vslot[c] * row_elems + vdg * 8);
+    }
+    load_slots(tile + 1);
   };
 
   auto stash = [&]() {
@@ -160,7 +167,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
       const int dg = piece - key * (D / 8);
       store16(&sm.k[key * KS + dg * 8], kreg[p]);
     }
-    if (vjob < VJOBS) {
+    if (vjob) {
       // Transpose 4 keys x 8 dims: each dim becomes 4 contiguous keys.
       const int pos = vpos(vkq * 4);
       const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
@@ -169,14 +176,10 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
                                 {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) ? 16 : 0;
-        const uint32_t k0 = (w[0][e >> 1] >> sh) & 0xffffu;
-        const uint32_t k1 = (w[1][e >> 1] >> sh) & 0xffffu;
-        const uint32_t k2 = (w[2][e >> 1] >> sh) & 0xffffu;
-        const uint32_t k3 = (w[3][e >> 1] >> sh) & 0xffffu;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         uint2 v;
-        v.x = k0 | (k1 << 16);
-        v.y = k2 | (k3 << 16);
+        v.x = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
+        v.y = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
         *reinterpret_cast<uint2 *>(&sm.vt[(vdg * 8 + e) * VS + pos]) = v;
       }
     }
@@ -187,76 +190,68 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
     for (int x = 0; x < 16; ++x) o[db][x] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
+  // Running max in raw score units (sm_scale > 0 keeps the order); this
+  // lane's share of the running sum (its half of the keys).
+  float m_run = kNegInf, l_lane = 0.f;
+  const float c2 = a.scale_log2;
+  const f32x16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                           0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
 
-  if (ntiles > 0) fetch(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();  // every wave is done reading the previous tile
-    stash();
-    __syncthreads();
-    if (tile + 1 < ntiles) fetch(tile + 1);
-
-    // S^T for the two 32-key blocks of the tile.
+  // One tile of 64 keys: S^T, (mask), online softmax, O^T += V^T P^T.
+  auto compute = [&](int tile, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
     f32x16_t sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int x = 0; x < 16; ++x) sacc[kb][x] = 0.f;
       const uint16_t *krow = &sm.k[(kb * 32 + col) * KS + 8 * half];
+      sacc[kb] = mfma32(*reinterpret_cast<const uint4 *>(krow), qf[0], zero16);
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const uint4 kf = *reinterpret_cast<const uint4 *>(krow + 16 * s);
-        sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
-      }
+      for (int s = 1; s < KSTEPS; ++s)
+        sacc[kb] = mfma32(*reinterpret_cast<const uint4 *>(krow + 16 * s), qf[s], sacc[kb]);
     }
-
-    // Scale to base 2, mask, online softmax over this lane's row.
-    const int kbase_idx = tile * BN;
-    const bool need_mask = kbase_idx + BN > wave_min_lim;
+    if constexpr (MASK) {
+      const int kbase_idx = tile * BN + 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x)
+          if (kbase_idx + kb * 32 + 8 * (x >> 2) + (x & 3) >= lim) sacc[kb][x] = kNegInf;
+    }
     float tmax = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        float v = sacc[kb][x] * a.scale_log2;
-        if (need_mask) {
-          const int key = kbase_idx + kb * 32 + 8 * (x >> 2) + 4 * half + (x & 3);
-          if (key >= lim) v = kNegInf;
-        }
-        sacc[kb][x] = v;
-        tmax = fmaxf(tmax, v);
-      }
+      for (int x = 0; x < 16; ++x) tmax = fmaxf(tmax, sacc[kb][x]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
-    const float mref = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - mref);
-    float psum = 0.f;
+    if (__any(m_new > m_run)) {  // rescale only when some row's max moved
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run - m_new) * c2);
+      l_lane *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float p = fast_exp2(sacc[kb][x] - mref);
-        sacc[kb][x] = p;
-        psum += p;
-      }
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) o[db][x] *= alpha;
-
-    // O^T += V^T P^T over the four 16-key steps of the tile.
+      for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == kNegInf) ? 0.f : m_run * c2;
+    // Per 16-key step: weights for those keys, rounded to bf16, then the PV
+    // products that consume them.
 #pragma unroll
     for (int ts = 0; ts < 4; ++ts) {
       const int kb = ts >> 1;
       const int x0 = 8 * (ts & 1);
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(sacc[kb][x0 + e], c2, -mc));
       uint4 pf;
-      pf.x = pack_bf16x2(sacc[kb][x0 + 0], sacc[kb][x0 + 1]);
-      pf.y = pack_bf16x2(sacc[kb][x0 + 2], sacc[kb][x0 + 3]);
-      pf.z = pack_bf16x2(sacc[kb][x0 + 4], sacc[kb][x0 + 5]);
-      pf.w = pack_bf16x2(sacc[kb][x0 + 6], sacc[kb][x0 + 7]);
+      pf.x = pack_bf16x2(p[0], p[1]);
+      pf.y = pack_bf16x2(p[2], p[3]);
+      pf.z = pack_bf16x2(p[4], p[5]);
+      pf.w = pack_bf16x2(p[6], p[7]);
+      // the row sum uses the same bf16 weights the PV product sees
+      l_lane = dot2_bf16(pf.x, kOnes, l_lane);
+      l_lane = dot2_bf16(pf.y, kOnes, l_lane);
+      l_lane = dot2_bf16(pf.z, kOnes, l_lane);
+      l_lane = dot2_bf16(pf.w, kOnes, l_lane);
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
         const uint4 vf =
@@ -264,9 +259,33 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
         o[db] = mfma32(vf, pf, o[db]);
       }
     }
+  };
+
+  // Tiles every row of the workgroup sees whole, then the diagonal tiles
+  // that need the causal / length mask (separate loops keep one code path
+  // per loop, which keeps the register allocation tight).
+  // The next tile's rows are fetched into registers while this one is used.
+  auto stage = [&](int tile) {
+    __syncthreads();  // every wave is done reading the previous tile
+    stash();
+    __syncthreads();
+    if (tile + 1 < ntiles) fetch(tile + 1);
+  };
+  if (ntiles > 0) {
+    load_slots(0);
+    fetch(0);
+  }
+  for (int tile = 0; tile < n_free; ++tile) {
+    stage(tile);
+    compute(tile, std::false_type{});
+  }
+  for (int tile = n_free; tile < ntiles; ++tile) {
+    stage(tile);
+    compute(tile, std::true_type{});
   }
 
   if (!row_ok) return;
+  const float l_run = l_lane + __shfl_xor(l_lane, 32);
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((int64_t)(q0 + t) * a.n_heads + h) * D;
 #pragma unroll
