@@ -12,12 +12,16 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 // fp32 -> bf16 bit pattern, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// Two fp32 -> one dword of two bf16 (lo in bits 0..15), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // a.lo*b.lo + a.hi*b.hi + c with bf16 pairs held in dwords (v_dot2_f32_bf16).

@@ -61,11 +61,13 @@ struct PrefillArgs {
   const int32_t *kv_indptr;
   const void *q;              // [n_new, n_heads, head_dim] bf16
   void *out;                  // [n_new, n_heads, head_dim] bf16
+  int64_t pool_size;          // slots per layer
   int32_t batch;
   int32_t n_heads;
   int32_t n_kv_heads;
   int32_t group;
   int32_t max_q_len;
+  int32_t row_blocks;         // row blocks per request in the launch (set by the launcher)
   int32_t causal;
   float scale_log2;
 };

@@ -279,6 +279,7 @@ pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_s
   a.kv_indptr = step->kv_indptr;
   a.q = q;
   a.out = out;
+  a.pool_size = pool->size;
   a.batch = step->batch;
   a.n_heads = n_heads;
   a.n_kv_heads = pool->n_kv_heads;

@@ -37,7 +37,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kNegInf = -INFINITY;
-constexpr int BM = 128;   // query rows per workgroup
+constexpr int NT = 256;   // threads per workgroup (4 wavefronts)
+constexpr int BM = NT / 64 * 32;  // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
 constexpr int WROWS = 32; // query rows per wavefront
 
@@ -64,26 +65,35 @@ struct Smem {
   uint16_t vt[D * VS];
 };
 
-template <int D>
-__global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
+// OFF32: every row of the layer lies within 4 GiB of the layer base, so row
+// addresses are a uniform 64-bit base plus a 32-bit byte offset.
+template <int D, bool OFF32>
+__global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   constexpr int KS = Smem<D>::KS;
   constexpr int VS = Smem<D>::VS;
   constexpr int KSTEPS = D / 16;             // MFMA steps over head_dim for S^T
   constexpr int DBLK = D / 32;               // 32-dim blocks of O^T
-  constexpr int KPIECES = BN * D / 8 / 256;  // 16-byte K pieces per thread per tile
+  constexpr int KPIECES = BN * D / 8 / NT;   // 16-byte K pieces per thread per tile
   constexpr int VJOBS = (BN / 4) * (D / 8);  // (4-key, 8-dim) V jobs per tile
-  __shared__ Smem<D> sm;
+  __shared__ Smem<D> sm[2];  // tile n is used from one while tile n+1 is staged into the other
 
-  const int i = blockIdx.z;
-  const int hk = blockIdx.y;
+  // Workgroups are dispatched to the 8 XCDs round-robin by linear id; taking
+  // the kv-head from the low part of the id keeps every workgroup of one
+  // kv-head on the same XCD (for 8 kv-heads), so the row blocks of a request
+  // share that head's K/V rows in one L2.
+  const int lin = blockIdx.x;
+  const int hk = lin % a.n_kv_heads;
+  const int rest = lin / a.n_kv_heads;
+  const int i = rest / a.row_blocks;
+  const int bx = rest - i * a.row_blocks;
   const int G = a.group;
   const int q0 = a.qo_indptr[i];
   const int q_len = a.qo_indptr[i + 1] - q0;
   const int kv_len = a.kv_indptr[i + 1] - a.kv_indptr[i];
   const int rows = q_len * G;
   const int nblk = (rows + BM - 1) / BM;
-  if ((int)blockIdx.x >= nblk) return;
-  const int rb = nblk - 1 - (int)blockIdx.x;  // heaviest row block first
+  if (bx >= nblk) return;
+  const int rb = nblk - 1 - bx;  // heaviest row block first
   const int prefix = kv_len - q_len;
 
   const int tid = threadIdx.x;
@@ -119,9 +129,15 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
   }
 
   const int32_t *table = a.req_to_token + (int64_t)a.req_pool_indices[i] * a.max_ctx_len;
-  const int64_t row_elems = (int64_t)a.n_kv_heads * D;
-  const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k_layer) + (int64_t)hk * D;
-  const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v_layer) + (int64_t)hk * D;
+  const uint32_t row_bytes = (uint32_t)a.n_kv_heads * D * 2;
+  const char *kbase = reinterpret_cast<const char *>(a.k_layer) + (int64_t)hk * D * 2;
+  const char *vbase = reinterpret_cast<const char *>(a.v_layer) + (int64_t)hk * D * 2;
+  auto row_addr = [&](const char *base, int slot, uint32_t col_bytes) -> const char * {
+    if constexpr (OFF32)
+      return base + ((uint32_t)slot * row_bytes + col_bytes);
+    else
+      return base + ((int64_t)slot * row_bytes + col_bytes);
+  };
 
   // Global -> register staging of one tile.  K: 16 lanes cover one key row.
   // V: lanes first run over the 16 key quads of the tile, so that the
@@ -136,36 +152,34 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
   // tile's K/V loads never wait on a table load.  Keys past kv_end read the
   // last valid key instead (always masked), keeping every load unconditional.
   int kslot[KPIECES], vslot[4];
+  auto slot_of = [&](int j) { return table[(uint32_t)min(j, kv_end - 1)]; };
   auto load_slots = [&](int tile) {
     const int base = tile * BN;
 #pragma unroll
-    for (int p = 0; p < KPIECES; ++p) {
-      const int key = (tid + 256 * p) / (D / 8);
-      kslot[p] = table[min(base + key, kv_end - 1)];
-    }
+    for (int p = 0; p < KPIECES; ++p) kslot[p] = slot_of(base + (tid + NT * p) / (D / 8));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vslot[c] = table[min(base + vkq * 4 + c, kv_end - 1)];
+    for (int c = 0; c < 4; ++c) vslot[c] = slot_of(base + vkq * 4 + c);
   };
   auto fetch = [&](int tile) {
 #pragma unroll
     for (int p = 0; p < KPIECES; ++p) {
-      const int dg = (tid + 256 * p) % (D / 8);
-      kreg[p] = load16(kbase + (int64_t)kslot[p] * row_elems + dg * 8);
+      const uint32_t dg = (tid + NT * p) % (D / 8);
+      kreg[p] = load16(row_addr(kbase, kslot[p], dg * 16));
     }
     if (vjob) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) vreg[c] = load16(vbase + (int64_t)vslot[c] * row_elems + vdg * 8);
+      for (int c = 0; c < 4; ++c) vreg[c] = load16(row_addr(vbase, vslot[c], vdg * 16));
     }
     load_slots(tile + 1);
   };
 
-  auto stash = [&]() {
+  auto stash = [&](Smem<D> &buf) {
 #pragma unroll
     for (int p = 0; p < KPIECES; ++p) {
-      const int piece = tid + 256 * p;
+      const int piece = tid + NT * p;
       const int key = piece / (D / 8);
       const int dg = piece - key * (D / 8);
-      store16(&sm.k[key * KS + dg * 8], kreg[p]);
+      store16(&buf.k[key * KS + dg * 8], kreg[p]);
     }
     if (vjob) {
       // Transpose 4 keys x 8 dims: each dim becomes 4 contiguous keys.
@@ -180,7 +194,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
         uint2 v;
         v.x = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
         v.y = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
-        *reinterpret_cast<uint2 *>(&sm.vt[(vdg * 8 + e) * VS + pos]) = v;
+        *reinterpret_cast<uint2 *>(&buf.vt[(vdg * 8 + e) * VS + pos]) = v;
       }
     }
   };
@@ -199,12 +213,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
   constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
 
   // One tile of 64 keys: S^T, (mask), online softmax, O^T += V^T P^T.
-  auto compute = [&](int tile, auto masked) {
+  auto compute = [&](int tile, const Smem<D> &buf, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
     f32x16_t sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint16_t *krow = &sm.k[(kb * 32 + col) * KS + 8 * half];
+      const uint16_t *krow = &buf.k[(kb * 32 + col) * KS + 8 * half];
       sacc[kb] = mfma32(*reinterpret_cast<const uint4 *>(krow), qf[0], zero16);
 #pragma unroll
       for (int s = 1; s < KSTEPS; ++s)
@@ -255,7 +269,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
         const uint4 vf =
-            *reinterpret_cast<const uint4 *>(&sm.vt[(db * 32 + col) * VS + 16 * ts + 8 * half]);
+            *reinterpret_cast<const uint4 *>(&buf.vt[(db * 32 + col) * VS + 16 * ts + 8 * half]);
         o[db] = mfma32(vf, pf, o[db]);
       }
     }
@@ -264,24 +278,31 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
   // Tiles every row of the workgroup sees whole, then the diagonal tiles
   // that need the causal / length mask (separate loops keep one code path
   // per loop, which keeps the register allocation tight).
-  // The next tile's rows are fetched into registers while this one is used.
-  auto stage = [&](int tile) {
-    __syncthreads();  // every wave is done reading the previous tile
-    stash();
-    __syncthreads();
-    if (tile + 1 < ntiles) fetch(tile + 1);
-  };
+  // Pipeline: tile n is multiplied from one LDS buffer while the registers
+  // holding tile n+1 are staged into the other and tile n+2's rows are
+  // fetched; one barrier per tile.  Tiles every row of the workgroup sees
+  // whole run a loop without mask code, the diagonal tiles a masked loop
+  // (one code path per loop keeps the register allocation tight).
   if (ntiles > 0) {
     load_slots(0);
     fetch(0);
+    stash(sm[0]);
+    if (ntiles > 1) fetch(1);
+    __syncthreads();
   }
+  auto advance = [&](int tile) {
+    if (tile + 1 < ntiles) stash(sm[(tile + 1) & 1]);
+    if (tile + 2 < ntiles) fetch(tile + 2);
+  };
   for (int tile = 0; tile < n_free; ++tile) {
-    stage(tile);
-    compute(tile, std::false_type{});
+    advance(tile);
+    compute(tile, sm[tile & 1], std::false_type{});
+    __syncthreads();
   }
   for (int tile = n_free; tile < ntiles; ++tile) {
-    stage(tile);
-    compute(tile, std::true_type{});
+    advance(tile);
+    compute(tile, sm[tile & 1], std::true_type{});
+    __syncthreads();
   }
 
   if (!row_ok) return;
@@ -305,13 +326,26 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(const PrefillArgs a) {
 hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, hipStream_t stream) {
   const int64_t row_blocks = ((int64_t)a.max_q_len * a.group + BM - 1) / BM;
   if (row_blocks > INT32_MAX) return hipErrorInvalidValue;
-  const dim3 grid((uint32_t)row_blocks, a.n_kv_heads, a.batch);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, stream, a);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, stream, a);
-  else
+  const int64_t blocks = row_blocks * a.n_kv_heads * a.batch;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  PrefillArgs args = a;
+  args.row_blocks = (int32_t)row_blocks;
+  const dim3 grid((uint32_t)blocks);
+  const uint64_t layer_bytes = (uint64_t)a.pool_size * a.n_kv_heads * head_dim * 2;
+  const bool off32 = layer_bytes <= 0xffffffffull;
+  if (head_dim == 128) {
+    if (off32)
+      hipLaunchKernelGGL((prefill_kernel<128, true>), grid, dim3(NT), 0, stream, args);
+    else
+      hipLaunchKernelGGL((prefill_kernel<128, false>), grid, dim3(NT), 0, stream, args);
+  } else if (head_dim == 64) {
+    if (off32)
+      hipLaunchKernelGGL((prefill_kernel<64, true>), grid, dim3(NT), 0, stream, args);
+    else
+      hipLaunchKernelGGL((prefill_kernel<64, false>), grid, dim3(NT), 0, stream, args);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
