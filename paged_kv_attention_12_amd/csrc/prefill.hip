@@ -142,11 +142,12 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   // Global -> register staging of one tile.  K: 16 lanes cover one key row.
   // V: lanes first run over the 16 key quads of the tile, so that the
   // transposed LDS writes of a 16-lane group fill 128 distinct bytes.
-  uint4 kreg[KPIECES];
-  uint4 vreg[4];
+  // Two register stages (A, B) alternate, so rows are fetched two tiles
+  // before they are staged into LDS.
+  uint4 kregA[KPIECES], vregA[4], kregB[KPIECES], vregB[4];
   const int vkq = tid & 15;  // keys 4 * vkq .. + 3
   const int vdg = tid >> 4;  // dims 8 * vdg .. + 7
-  const bool vjob = tid < VJOBS;
+  const bool vjob = VJOBS >= NT || tid < VJOBS;  // compile-time true for head_dim 128
 
   // Slot ids are loaded one tile ahead of the rows they address, so a
   // tile's K/V loads never wait on a table load.  Keys past kv_end read the
@@ -160,7 +161,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) vslot[c] = slot_of(base + vkq * 4 + c);
   };
-  auto fetch = [&](int tile) {
+  auto fetch = [&](int tile, uint4(&kreg)[KPIECES], uint4(&vreg)[4]) {
 #pragma unroll
     for (int p = 0; p < KPIECES; ++p) {
       const uint32_t dg = (tid + NT * p) % (D / 8);
@@ -173,7 +174,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
     load_slots(tile + 1);
   };
 
-  auto stash = [&](Smem<D> &buf) {
+  auto stash = [&](Smem<D> &buf, const uint4(&kreg)[KPIECES], const uint4(&vreg)[4]) {
 #pragma unroll
     for (int p = 0; p < KPIECES; ++p) {
       const int piece = tid + NT * p;
@@ -212,10 +213,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
                            0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
 
-  // One tile of 64 keys: S^T, (mask), online softmax, O^T += V^T P^T.
-  auto compute = [&](int tile, const Smem<D> &buf, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    f32x16_t sacc[2];
+  // S^T of one 64-key tile (two 32-key blocks).
+  auto qk = [&](const Smem<D> &buf, f32x16_t(&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const uint16_t *krow = &buf.k[(kb * 32 + col) * KS + 8 * half];
@@ -224,6 +223,11 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
       for (int s = 1; s < KSTEPS; ++s)
         sacc[kb] = mfma32(*reinterpret_cast<const uint4 *>(krow + 16 * s), qf[s], sacc[kb]);
     }
+  };
+
+  // (Mask,) online softmax of one tile's S^T, then O^T += V^T P^T.
+  auto softmax_pv = [&](int tile, f32x16_t(&sacc)[2], const Smem<D> &buf, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
     if constexpr (MASK) {
       const int kbase_idx = tile * BN + 4 * half;
 #pragma unroll
@@ -275,35 +279,45 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  // Tiles every row of the workgroup sees whole, then the diagonal tiles
-  // that need the causal / length mask (separate loops keep one code path
-  // per loop, which keeps the register allocation tight).
-  // Pipeline: tile n is multiplied from one LDS buffer while the registers
-  // holding tile n+1 are staged into the other and tile n+2's rows are
-  // fetched; one barrier per tile.  Tiles every row of the workgroup sees
-  // whole run a loop without mask code, the diagonal tiles a masked loop
-  // (one code path per loop keeps the register allocation tight).
+  // Pipeline, one barrier per tile: while tile n is multiplied from one LDS
+  // buffer, the register stage holding tile n+1 is staged into the other
+  // buffer and refilled with tile n+3; the other stage holds tile n+2 in
+  // flight.  Tiles every row of the workgroup sees whole run an unmasked
+  // step, the diagonal tiles a masked one (one code path per loop keeps the
+  // register allocation tight).
   if (ntiles > 0) {
     load_slots(0);
-    fetch(0);
-    stash(sm[0]);
-    if (ntiles > 1) fetch(1);
+    fetch(0, kregA, vregA);
+    stash(sm[0], kregA, vregA);
+    if (ntiles > 1) fetch(1, kregA, vregA);
+    if (ntiles > 2) fetch(2, kregB, vregB);
     __syncthreads();
   }
-  auto advance = [&](int tile) {
-    if (tile + 1 < ntiles) stash(sm[(tile + 1) & 1]);
-    if (tile + 2 < ntiles) fetch(tile + 2);
+  // The S^T products of tile n are issued first; the staging work for later
+  // tiles (V transpose, LDS writes, row fetches) then runs on the vector and
+  // memory units while the matrix cores work, followed by the softmax and PV
+  // products.  Staging past the last tile writes an LDS buffer no tile reads
+  // and reads clamped, valid rows: it is harmless and keeps the code
+  // straight-line for the scheduler.
+  auto step = [&](int tile, uint4(&kreg)[KPIECES], uint4(&vreg)[4], auto masked) {
+    f32x16_t sacc[2];
+    qk(sm[tile & 1], sacc);
+    stash(sm[(tile + 1) & 1], kreg, vreg);
+    fetch(tile + 3, kreg, vreg);
+    softmax_pv(tile, sacc, sm[tile & 1], masked);
+    __syncthreads();
   };
-  for (int tile = 0; tile < n_free; ++tile) {
-    advance(tile);
-    compute(tile, sm[tile & 1], std::false_type{});
-    __syncthreads();
+  const int n_free2 = n_free & ~1;
+  int tile = 0;
+  for (; tile < n_free2; tile += 2) {
+    step(tile, kregA, vregA, std::false_type{});
+    step(tile + 1, kregB, vregB, std::false_type{});
   }
-  for (int tile = n_free; tile < ntiles; ++tile) {
-    advance(tile);
-    compute(tile, sm[tile & 1], std::true_type{});
-    __syncthreads();
+  for (; tile + 1 < ntiles; tile += 2) {
+    step(tile, kregA, vregA, std::true_type{});
+    step(tile + 1, kregB, vregB, std::true_type{});
   }
+  if (tile < ntiles) step(tile, kregA, vregA, std::true_type{});
 
   if (!row_ok) return;
   const float l_run = l_lane + __shfl_xor(l_lane, 32);
