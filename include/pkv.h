@@ -79,6 +79,9 @@ typedef struct {
   int64_t n_new;                    /* total new tokens (decode: batch)                */
   int32_t max_len;                  /* max(seq_lens)                                   */
   int32_t max_q_len;                /* max(q_lens) (decode: 1)                         */
+  const int32_t *prefill_order;     /* [batch] or NULL: order in which prefill takes the
+                                       requests (a permutation of 0..batch-1, e.g. the
+                                       one pkv_build_step returns); affects speed only */
 } pkv_step;
 
 /* Human-readable name of a status. Never NULL. */
@@ -101,7 +104,10 @@ int32_t pkv_last_hip_error(void);
  * req_to_token[r_b, seq_len_b - q_len_b + t].
  * Outputs: kv_indptr[batch+1], qo_indptr[batch+1], out_cache_loc (capacity
  * out_cache_loc_cap entries, filled in qo order), *n_new, *max_len,
- * *max_q_len.  Returns PKV_ERR_BAD_METADATA (outputs unspecified) when a
+ * *max_q_len, and, when prefill_order is not NULL, prefill_order[batch]: the
+ * requests sorted by seq_len, longest first (ties in batch order), a
+ * processing order for pkv_paged_prefill that starts the heaviest work
+ * first.  Returns PKV_ERR_BAD_METADATA (outputs unspecified) when a
  * row, length or new-token count is out of range, PKV_ERR_SHAPE when
  * out_cache_loc_cap is too small.
  * ---------------------------------------------------------------------- */
@@ -111,7 +117,7 @@ pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices,
                           int64_t max_ctx_len, int32_t *kv_indptr,
                           int32_t *qo_indptr, int32_t *out_cache_loc,
                           int64_t out_cache_loc_cap, int64_t *n_new,
-                          int32_t *max_len, int32_t *max_q_len);
+                          int32_t *max_len, int32_t *max_q_len, int32_t *prefill_order);
 
 /* Checked mode: validates HOST copies of one step's metadata against a pool
  * of `size` slots.  Accepts (PKV_OK) iff every request row is in
@@ -120,12 +126,14 @@ pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices,
  * lengths (qo_indptr NULL means decode: q_len 1 each), every slot read
  * (req_to_token[r_b, 0 .. seq_len_b-1]) lies in [0, size), the write slots
  * are pairwise distinct, in [0, size), and equal the table entry of their
- * token's logical position.  Else PKV_ERR_BAD_METADATA. */
+ * token's logical position, and prefill_order (NULL: not checked) is a
+ * permutation of 0..batch-1.  Else PKV_ERR_BAD_METADATA. */
 pkv_status pkv_validate_step(int64_t size, int64_t num_reqs, int64_t max_ctx_len,
                              const int32_t *req_to_token, int32_t batch,
                              const int32_t *req_pool_indices, const int32_t *seq_lens,
                              const int32_t *kv_indptr, const int32_t *qo_indptr,
-                             const int32_t *out_cache_loc, int64_t n_new);
+                             const int32_t *out_cache_loc, int64_t n_new,
+                             const int32_t *prefill_order);
 
 /* ------------------------------------------------------------------------
  * K/V write ("Inference" guide, section "KVCache System": the attention layer

@@ -34,10 +34,12 @@ class DeviceStep:
         self.qo_indptr = to(md["qo_indptr"])
         self.out_cache_loc = to(md["out_cache_loc"]) if self.n_new else \
             torch.zeros(0, dtype=torch.int32, device=device)
+        self.prefill_order = to(md["prefill_order"]) if self.batch else None
         self.c = B.make_step(self.batch, self.req_pool_indices, self.seq_lens, self.kv_indptr,
                              None if self.decode else self.qo_indptr,
                              self.out_cache_loc if self.n_new else None, self.n_new,
-                             self.max_len, self.max_q_len)
+                             self.max_len, self.max_q_len,
+                             None if self.decode else self.prefill_order)
 
 
 def decode_workspace(batch: int, n_heads: int, head_dim: int, num_splits: int, device="cuda"):

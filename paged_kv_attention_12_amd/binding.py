@@ -56,6 +56,7 @@ class pkv_step(C.Structure):
         ("batch", C.c_int32), ("req_pool_indices", C.c_void_p), ("seq_lens", C.c_void_p),
         ("kv_indptr", C.c_void_p), ("qo_indptr", C.c_void_p), ("out_cache_loc", C.c_void_p),
         ("n_new", C.c_int64), ("max_len", C.c_int32), ("max_q_len", C.c_int32),
+        ("prefill_order", C.c_void_p),
     ]
 
 
@@ -84,8 +85,8 @@ def load() -> C.CDLL:
     sig = {
         "pkv_status_string": (C.c_char_p, [C.c_int]),
         "pkv_last_hip_error": (i32, []),
-        "pkv_build_step": (C.c_int, [i32, P, P, P, P, i64, i64, P, P, P, i64, P, P, P]),
-        "pkv_validate_step": (C.c_int, [i64, i64, i64, P, i32, P, P, P, P, P, i64]),
+        "pkv_build_step": (C.c_int, [i32, P, P, P, P, i64, i64, P, P, P, i64, P, P, P, P]),
+        "pkv_validate_step": (C.c_int, [i64, i64, i64, P, i32, P, P, P, P, P, i64, P]),
         "pkv_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, P, i64, P]),
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "pkv_decode_pick_splits": (i32, [i32, i32, i32, i32, i64, i32]),
@@ -180,7 +181,7 @@ def make_pool(k_buffer, v_buffer, req_to_token) -> pkv_pool:
 
 def make_step(batch: int, req_pool_indices, seq_lens, kv_indptr=None, qo_indptr=None,
               out_cache_loc=None, n_new: Optional[int] = None, max_len: int = 0,
-              max_q_len: int = 1) -> pkv_step:
+              max_q_len: int = 1, prefill_order=None) -> pkv_step:
     """pkv_step view of device int32 tensors plus the host scalars."""
     import torch
     s = pkv_step()
@@ -193,6 +194,7 @@ def make_step(batch: int, req_pool_indices, seq_lens, kv_indptr=None, qo_indptr=
     s.n_new = int(batch if n_new is None else n_new)
     s.max_len = int(max_len)
     s.max_q_len = int(max_q_len)
+    s.prefill_order = _dev_ptr(prefill_order, "prefill_order", torch.int32)
     return s
 
 
@@ -215,17 +217,19 @@ def pkv_build_step(req_pool_indices, seq_lens, req_to_token, q_lens=None) -> dic
     kv = np.zeros(B + 1, dtype=np.int32)
     qo = np.zeros(B + 1, dtype=np.int32)
     loc = np.zeros(max(cap, 1), dtype=np.int32)
+    order = np.zeros(max(B, 1), dtype=np.int32)
     n_new, ml, mq = C.c_int64(0), C.c_int32(0), C.c_int32(0)
     st = load().pkv_build_step(B, _hp(rpi), _hp(sl), _hp(ql), _hp(table), table.shape[0],
                                table.shape[1], _hp(kv), _hp(qo), _hp(loc), cap,
-                               C.byref(n_new), C.byref(ml), C.byref(mq))
+                               C.byref(n_new), C.byref(ml), C.byref(mq), _hp(order))
     _check(st, "pkv_build_step")
     return {"kv_indptr": kv, "qo_indptr": qo, "out_cache_loc": loc[:n_new.value].copy(),
-            "n_new": n_new.value, "max_len": ml.value, "max_q_len": mq.value}
+            "n_new": n_new.value, "max_len": ml.value, "max_q_len": mq.value,
+            "prefill_order": order[:B].copy()}
 
 
 def pkv_validate_step(size: int, req_to_token, req_pool_indices, seq_lens, kv_indptr,
-                      qo_indptr, out_cache_loc) -> int:
+                      qo_indptr, out_cache_loc, prefill_order=None) -> int:
     """Checked mode on host copies; returns the status (0 = well formed)."""
     table = _host_i32(req_to_token, "req_to_token")
     rpi = _host_i32(req_pool_indices, "req_pool_indices")
@@ -233,12 +237,15 @@ def pkv_validate_step(size: int, req_to_token, req_pool_indices, seq_lens, kv_in
     kv = _host_i32(kv_indptr, "kv_indptr")
     qo = _host_i32(qo_indptr, "qo_indptr")
     loc = _host_i32(out_cache_loc, "out_cache_loc")
+    order = _host_i32(prefill_order, "prefill_order")
     B = len(sl)
+    if order is not None and len(order) != B:
+        return PKV_ERR_BAD_METADATA
     if len(rpi) != B or len(kv) != B + 1 or (qo is not None and len(qo) != B + 1):
         return PKV_ERR_BAD_METADATA
     return int(load().pkv_validate_step(int(size), table.shape[0], table.shape[1], _hp(table),
                                         B, _hp(rpi), _hp(sl), _hp(kv), _hp(qo), _hp(loc),
-                                        0 if loc is None else len(loc)))
+                                        0 if loc is None else len(loc), _hp(order)))
 
 
 def pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, k_new, v_new,

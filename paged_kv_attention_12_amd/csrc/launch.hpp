@@ -59,6 +59,7 @@ struct PrefillArgs {
   const int32_t *req_pool_indices;
   const int32_t *qo_indptr;
   const int32_t *kv_indptr;
+  const int32_t *order;       // [batch] request processing order, or null
   const void *q;              // [n_new, n_heads, head_dim] bf16
   void *out;                  // [n_new, n_heads, head_dim] bf16
   int64_t pool_size;          // slots per layer

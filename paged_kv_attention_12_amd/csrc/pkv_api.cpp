@@ -74,7 +74,7 @@ pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices, const 
                           const int32_t *q_lens, const int32_t *req_to_token, int64_t num_reqs,
                           int64_t max_ctx_len, int32_t *kv_indptr, int32_t *qo_indptr,
                           int32_t *out_cache_loc, int64_t out_cache_loc_cap, int64_t *n_new,
-                          int32_t *max_len, int32_t *max_q_len) {
+                          int32_t *max_len, int32_t *max_q_len, int32_t *prefill_order) {
   if (batch < 0) return PKV_ERR_SHAPE;
   if (!kv_indptr || !qo_indptr || !n_new || !max_len || !max_q_len) return PKV_ERR_NULL;
   if (batch > 0 && (!req_pool_indices || !seq_lens || !req_to_token)) return PKV_ERR_NULL;
@@ -103,6 +103,12 @@ pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices, const 
   *n_new = qo;
   *max_len = ml;
   *max_q_len = mq;
+  if (prefill_order) {
+    // longest context first; ties keep batch order
+    for (int32_t b = 0; b < batch; ++b) prefill_order[b] = b;
+    std::stable_sort(prefill_order, prefill_order + batch,
+                     [&](int32_t x, int32_t y) { return seq_lens[x] > seq_lens[y]; });
+  }
   return PKV_OK;
 }
 
@@ -110,7 +116,8 @@ pkv_status pkv_validate_step(int64_t size, int64_t num_reqs, int64_t max_ctx_len
                              const int32_t *req_to_token, int32_t batch,
                              const int32_t *req_pool_indices, const int32_t *seq_lens,
                              const int32_t *kv_indptr, const int32_t *qo_indptr,
-                             const int32_t *out_cache_loc, int64_t n_new) {
+                             const int32_t *out_cache_loc, int64_t n_new,
+                             const int32_t *prefill_order) {
   if (batch < 0 || size <= 0 || num_reqs <= 0 || max_ctx_len <= 0) return PKV_ERR_SHAPE;
   if (batch == 0) return n_new == 0 ? PKV_OK : PKV_ERR_BAD_METADATA;
   if (!req_to_token || !req_pool_indices || !seq_lens || !kv_indptr) return PKV_ERR_NULL;
@@ -136,6 +143,14 @@ pkv_status pkv_validate_step(int64_t size, int64_t num_reqs, int64_t max_ctx_len
       if (loc < 0 || loc >= size) return PKV_ERR_BAD_METADATA;
       if (!seen.insert(loc).second) return PKV_ERR_BAD_METADATA;
       if (loc != row[L - ql + t]) return PKV_ERR_BAD_METADATA;
+    }
+  }
+  if (prefill_order) {
+    std::vector<char> hit((size_t)batch, 0);
+    for (int32_t b = 0; b < batch; ++b) {
+      const int32_t x = prefill_order[b];
+      if (x < 0 || x >= batch || hit[(size_t)x]) return PKV_ERR_BAD_METADATA;
+      hit[(size_t)x] = 1;
     }
   }
   return PKV_OK;
@@ -277,6 +292,7 @@ pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_s
   a.req_pool_indices = step->req_pool_indices;
   a.qo_indptr = step->qo_indptr;
   a.kv_indptr = step->kv_indptr;
+  a.order = step->prefill_order;
   a.q = q;
   a.out = out;
   a.pool_size = pool->size;

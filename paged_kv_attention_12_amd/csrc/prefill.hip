@@ -84,8 +84,11 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   const int lin = blockIdx.x;
   const int hk = lin % a.n_kv_heads;
   const int rest = lin / a.n_kv_heads;
-  const int i = rest / a.row_blocks;
-  const int bx = rest - i * a.row_blocks;
+  // Requests go in the caller's order (longest context first when it passes
+  // one), each request's row blocks together so they share L2.
+  const int ri = rest / a.row_blocks;
+  const int bx = rest - ri * a.row_blocks;
+  const int i = a.order ? a.order[ri] : ri;
   const int G = a.group;
   const int q0 = a.qo_indptr[i];
   const int q_len = a.qo_indptr[i + 1] - q0;

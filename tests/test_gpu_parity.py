@@ -262,3 +262,17 @@ def test_prefill_q_len_one_matches_decode_oracle():
     np.testing.assert_allclose(ref, dec, rtol=0, atol=1e-12)
     out = gpu_prefill(case, t)
     assert_close(to_np(out), ref, "bf16", "q_len 1")
+
+
+def test_prefill_order_changes_nothing_but_schedule():
+    case = W.random_case(301, [700, 40, 2500, 9], [300, 40, 100, 9], n_heads=32, n_kv_heads=8,
+                         head_dim=128, dtype="bf16")
+    t = W.make_tensors(case, device="cuda")
+    step = api.DeviceStep(case.req_pool_indices, case.seq_lens, case.req_to_token, case.q_lens)
+    assert step.host["prefill_order"].tolist() == [2, 0, 1, 3]
+    o1 = api.prefill_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, step, t["q"],
+                          t["k_new"], t["v_new"], case.sm_scale).clone()
+    step.c.prefill_order = None   # natural order
+    o2 = api.prefill_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, step, t["q"],
+                          t["k_new"], t["v_new"], case.sm_scale, write_kv=False)
+    assert torch.equal(o1, o2)

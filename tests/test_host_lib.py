@@ -49,7 +49,7 @@ def test_build_step_golden(lib):
     g = json.load(open(os.path.join(GOLDEN, "step_metadata.json")))
     md = B.pkv_build_step(g["req_pool_indices"], g["seq_lens"], np.array(g["req_to_token"]),
                           g["q_lens"])
-    for k in ("kv_indptr", "qo_indptr", "out_cache_loc"):
+    for k in ("kv_indptr", "qo_indptr", "out_cache_loc", "prefill_order"):
         assert md[k].tolist() == g[k]
     assert (md["n_new"], md["max_len"], md["max_q_len"]) == (g["n_new"], g["max_len"],
                                                              g["max_q_len"])
@@ -66,7 +66,7 @@ def test_build_step_matches_oracle_bitwise(lib, maker):
     ql = None if case.is_decode else case.q_lens
     got = B.pkv_build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, ql)
     ref = oracle.build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, ql)
-    for k in ("kv_indptr", "qo_indptr", "out_cache_loc"):
+    for k in ("kv_indptr", "qo_indptr", "out_cache_loc", "prefill_order"):
         assert got[k].dtype == np.int32
         assert got[k].tobytes() == ref[k].tobytes(), k
     for k in ("n_new", "max_len", "max_q_len"):
@@ -112,6 +112,17 @@ def test_validate_step_agrees_with_oracle(lib):
     x = md["qo_indptr"].copy(); x[1] = 5; corrupt.append(dict(qo_indptr=x))
     for c in corrupt:
         assert _validate_both(case, md, **c) == (False, False), list(c)
+
+
+def test_validate_checks_prefill_order(lib):
+    case = W.random_case(62, [4, 9, 6], [1, 3, 6], n_heads=4, n_kv_heads=2, head_dim=64)
+    md = B.pkv_build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, case.q_lens)
+    args = (case.size, case.req_to_token, case.req_pool_indices, case.seq_lens, md["kv_indptr"],
+            md["qo_indptr"], md["out_cache_loc"])
+    assert md["prefill_order"].tolist() == [1, 2, 0]
+    assert B.pkv_validate_step(*args, prefill_order=md["prefill_order"]) == B.PKV_OK
+    for bad in ([1, 1, 0], [0, 1, 3], [2, 1], [-1, 0, 1]):
+        assert B.pkv_validate_step(*args, prefill_order=np.array(bad)) == B.PKV_ERR_BAD_METADATA
 
 
 def test_validate_decode_with_null_qo_indptr(lib):

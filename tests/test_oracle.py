@@ -372,7 +372,7 @@ def test_build_step_hand_worked_golden():
     g = json.load(open(os.path.join(GOLDEN, "step_metadata.json")))
     md = oracle.build_step(g["req_pool_indices"], g["seq_lens"], np.array(g["req_to_token"]),
                            g["q_lens"])
-    for key in ("kv_indptr", "qo_indptr", "out_cache_loc"):
+    for key in ("kv_indptr", "qo_indptr", "out_cache_loc", "prefill_order"):
         assert md[key].tolist() == g[key], key
         assert md[key].dtype == np.int32
     for key in ("max_len", "max_q_len", "n_new"):
