@@ -363,10 +363,6 @@ def main():
     from paged_kv_attention_12_amd import binding as B
     B.load()
 
-    if args.only_prefill:
-        print(json.dumps(bench_prefill()), flush=True)
-        return
-
     if args.copy_calibration:
         # A plain copy of known size: its HBM counters give the scale between
         # counter units and bytes on this machine.
@@ -378,6 +374,10 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies (read 1 GiB + write 1 GiB each)")
         del src, dst
+
+    if args.only_prefill:
+        print(json.dumps(bench_prefill()), flush=True)
+        return
 
     # ---- headline: Llama-3-8B-shaped B=1 decode, seq_len 32768 ----
     L_head = W.LLAMA_SWEEP[-1]
