@@ -239,49 +239,60 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
 }
 
 // One workgroup per (request, head) row.  The splits are spread over
-// 256 / (D/4) split groups of D/4 threads (4 dims each) so that many partial
-// loads are in flight; the groups' sums are then added through LDS.
+// 256 / (D/4) split groups of D/4 threads (4 dims each).  Each thread loads
+// (m, l, o) of up to KB splits in one batch, the row maximum is reduced over
+// the workgroup, then every thread weighs what it holds: one memory round
+// trip for up to SG * KB splits.  Group sums are added through LDS.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(const MergeArgs a) {
   constexpr int TPR = D / 4;
   constexpr int SG = 256 / TPR;
-  __shared__ float s_red[8];
+  constexpr int KB = 16;
+  __shared__ float s_red[4];
   __shared__ float4 s_num[SG][TPR];
   __shared__ float s_den[SG];
   const int r = blockIdx.x;
   const int t = threadIdx.x;
   const int S = a.num_splits;
-  const float *ml = a.ml_part + (int64_t)r * S * 2;
-  const float *op = a.o_part + (int64_t)r * S * D;
-
-  // M = max over non-empty splits
-  float M = kNegInf;
-  for (int s = t; s < S; s += 256)
-    if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
-  if ((t & 63) == 0) s_red[t >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  const float Mr = (M == kNegInf) ? 0.f : M;
-
   const int sg = t / TPR;
   const int c = t - sg * TPR;
+  const float *ml = a.ml_part + (int64_t)r * S * 2;
+  const float *op = a.o_part + (int64_t)r * S * D + c * 4;
+
   float den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  // KB splits per thread per batch: all their loads are issued before any is
-  // used, so a batch costs one memory round trip.
-  constexpr int KB = 16;
+  float M = kNegInf;  // running maximum over the batches seen so far
   for (int s0 = sg; s0 < S; s0 += SG * KB) {
     float4 ov[KB];
     float mv[KB], lv[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const int s = min(s0 + SG * k, S - 1);
-      ov[k] = *reinterpret_cast<const float4 *>(op + (int64_t)s * D + c * 4);
+      ov[k] = *reinterpret_cast<const float4 *>(op + (int64_t)s * D);
       mv[k] = ml[2 * s];
       lv[k] = (s0 + SG * k < S) ? ml[2 * s + 1] : 0.f;
     }
+    // maximum over this batch's non-empty splits, across the workgroup
+    float bm = M;
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+      if (lv[k] > 0.f) bm = fmaxf(bm, mv[k]);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) bm = fmaxf(bm, __shfl_xor(bm, x));
+    __syncthreads();  // s_red of the previous batch has been read
+    if ((t & 63) == 0) s_red[t >> 6] = bm;
+    __syncthreads();
+    const float Mn = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float Mr = (Mn == kNegInf) ? 0.f : Mn;
+    if (Mn != M && M != kNegInf) {  // earlier batches were weighed against M
+      const float f = fast_exp2(M - Mr);
+      den *= f;
+      num.x *= f;
+      num.y *= f;
+      num.z *= f;
+      num.w *= f;
+    }
+    M = Mn;
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const float w = lv[k] > 0.f ? lv[k] * fast_exp2(mv[k] - Mr) : 0.f;
