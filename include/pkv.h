@@ -223,7 +223,8 @@ pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_d
  * context); with causal == 0 it attends all kv_len_i keys.  QK^T and PV run
  * as bf16 matrix-core tiles with fp32 accumulation; the softmax weights are
  * rounded to bf16 before the PV product.  Uses step->max_q_len (host) to
- * size the launch.  Only PKV_BF16 pools are accepted (else PKV_ERR_DTYPE).
+ * size the launch.  Only PKV_BF16 pools are accepted (else PKV_ERR_DTYPE);
+ * sm_scale must be finite and > 0 (else PKV_ERR_SHAPE).
  * ---------------------------------------------------------------------- */
 pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,
                              const void *q, int32_t n_heads, float sm_scale,

@@ -280,7 +280,8 @@ pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_s
   if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || step->batch > 65535)
     return PKV_ERR_SHAPE;
   if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
-  if (!std::isfinite(sm_scale)) return PKV_ERR_SHAPE;
+  // the kernel ranks raw scores (the scale is applied in the exponent)
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f)) return PKV_ERR_SHAPE;
   if (step->batch == 0 || step->n_new == 0) return PKV_OK;
   if (!step->req_pool_indices || !step->qo_indptr || !step->kv_indptr) return PKV_ERR_NULL;
   if (step->max_q_len <= 0 || step->max_q_len > pool->max_ctx_len) return PKV_ERR_SHAPE;

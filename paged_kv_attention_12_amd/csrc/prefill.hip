@@ -8,7 +8,7 @@
 // and with the causal mask it sees keys 0 .. p_i + t.  Each output row is
 // o = sum_j softmax_j(q . k_j * sm_scale) v_j (section "KV Cache").
 //
-// Tiling.  A workgroup (4 wavefronts) owns one (request, kv-head, block of 128
+// Tiling.  A workgroup (8 wavefronts) owns one (request, kv-head, block of 256
 // query rows), where the rows of a request enumerate (token t, head g of the
 // kv-head's group) as r = t * G + g, so all G query heads sharing a kv-head
 // reuse one K/V tile and any group size works.  Each wavefront owns 32 rows.
@@ -20,8 +20,14 @@
 //                               taken straight from the S^T accumulators.
 // With S^T in this orientation every lane holds one query row, so the
 // online-softmax row max / row sum need one cross-lane step (lane l ^ 32).
-// The next tile's K/V rows are fetched into registers while the current tile
-// is being multiplied.
+//
+// Schedule.  A SIMD holds two wavefronts of the workgroup, one from each of
+// two groups (waves 0-3 and 4-7).  Both run the same tile pipeline, rotated
+// by half a tile: while one is in its matrix-core phase (S^T products) the
+// other is in its vector phase (softmax), so the two phases overlap on the
+// SIMD instead of both waves waiting on the same unit.  One barrier per tile;
+// tile n lives in LDS buffer n % 3 because the second group still reads tile
+// n-1 while tile n+1 is being staged.
 #include <math.h>
 
 #include <type_traits>
@@ -37,10 +43,12 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kNegInf = -INFINITY;
-constexpr int NT = 256;   // threads per workgroup (4 wavefronts)
-constexpr int BM = NT / 64 * 32;  // query rows per workgroup
-constexpr int BN = 64;    // keys per tile
-constexpr int WROWS = 32; // query rows per wavefront
+constexpr int NT = 512;              // threads per workgroup (8 wavefronts)
+constexpr int BN = 64;               // keys per tile
+constexpr int WROWS = 32;            // query rows per wavefront
+constexpr int BM = NT / 64 * WROWS;  // query rows per workgroup
+constexpr int NBUF = 3;              // LDS tile buffers
+constexpr float kSlack = 8.f;        // log2 headroom before the running max is raised
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) {
   return __builtin_bit_cast(bf16x8_t, v);
@@ -48,6 +56,14 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) {
 
 __device__ __forceinline__ f32x16_t mfma32(const uint4 &a, const uint4 &b, const f32x16_t &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Workgroup barrier that orders LDS accesses only: the global loads in
+// flight (rows fetched for later tiles) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Position of key k of a 64-key tile inside a transposed V row: bits 2 and 3 of
@@ -75,7 +91,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   constexpr int DBLK = D / 32;               // 32-dim blocks of O^T
   constexpr int KPIECES = BN * D / 8 / NT;   // 16-byte K pieces per thread per tile
   constexpr int VJOBS = (BN / 4) * (D / 8);  // (4-key, 8-dim) V jobs per tile
-  __shared__ Smem<D> sm[2];  // tile n is used from one while tile n+1 is staged into the other
+  static_assert(KPIECES >= 1 && VJOBS % 64 == 0 && VJOBS <= NT / 2, "staging split");
+  __shared__ Smem<D> sm[NBUF];
 
   // Workgroups are dispatched to the 8 XCDs round-robin by linear id; taking
   // the kv-head from the low part of the id keeps every workgroup of one
@@ -101,20 +118,19 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // This lane's query row (column of S^T / O^T).
+  // This lane's query row (column of S^T / O^T) and the keys it sees.
   const int r = rb * BM + wave * WROWS + col;
   const bool row_ok = r < rows;
   const int t = row_ok ? r / G : 0;
-  const int g = row_ok ? r - t * G : 0;
-  const int h = hk * G + g;
-  // Keys visible to this row.
+  const int h = hk * G + (row_ok ? r - t * G : 0);
   const int lim = !row_ok ? 0 : (a.causal ? prefix + t + 1 : kv_len);
 
   // Keys any row of the workgroup sees, and the tiles every row sees whole.
+  // A workgroup that gets here has at least one row, so ntiles >= 1.
   const int r_last = min(rows, (rb + 1) * BM) - 1;
   const int kv_end = a.causal ? min(kv_len, prefix + r_last / G + 1) : kv_len;
   const int ntiles = (kv_end + BN - 1) / BN;
@@ -124,8 +140,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   // Q (B operand of S^T): lane holds dims 16s + 8*half .. +8 of its row for step s.
   uint4 qf[KSTEPS];
   {
-    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) +
-                           ((int64_t)(q0 + t) * a.n_heads + h) * D + 8 * half;
+    const uint16_t *qrow =
+        reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(q0 + t) * a.n_heads + h) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
       qf[s] = row_ok ? load16(qrow + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
@@ -142,29 +158,35 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
       return base + ((int64_t)slot * row_bytes + col_bytes);
   };
 
-  // Global -> register staging of one tile.  K: 16 lanes cover one key row.
-  // V: lanes first run over the 16 key quads of the tile, so that the
-  // transposed LDS writes of a 16-lane group fill 128 distinct bytes.
-  // Two register stages (A, B) alternate, so rows are fetched two tiles
-  // before they are staged into LDS.
-  uint4 kregA[KPIECES], vregA[4], kregB[KPIECES], vregB[4];
+  // Global -> register staging of one tile.  K: every thread, 16 lanes per
+  // key row.  V: the first VJOBS threads (all in the first group: its
+  // staging sits in its matrix phase), lanes first running over the 16 key
+  // quads of the tile so that the transposed LDS writes of a 16-lane group
+  // fill 128 distinct bytes.
+  uint4 kreg[KPIECES], vreg[4];
   const int vkq = tid & 15;  // keys 4 * vkq .. + 3
   const int vdg = tid >> 4;  // dims 8 * vdg .. + 7
-  const bool vjob = VJOBS >= NT || tid < VJOBS;  // compile-time true for head_dim 128
+  const bool vjob = wave < VJOBS / 64;
 
   // Slot ids are loaded one tile ahead of the rows they address, so a
-  // tile's K/V loads never wait on a table load.  Keys past kv_end read the
-  // last valid key instead (always masked), keeping every load unconditional.
+  // tile's K/V loads never wait on a table load.  They are issued before the
+  // rows of the current fetch: the memory counter drains in issue order, so
+  // the next fetch's wait for its slot ids leaves these rows in flight.  Keys
+  // past kv_end read the last valid key instead (always masked), keeping
+  // every load unconditional.
   int kslot[KPIECES], vslot[4];
   auto slot_of = [&](int j) { return table[(uint32_t)min(j, kv_end - 1)]; };
-  auto load_slots = [&](int tile) {
+  auto load_slots = [&](int tile, int(&ks)[KPIECES], int(&vs)[4]) {
     const int base = tile * BN;
 #pragma unroll
-    for (int p = 0; p < KPIECES; ++p) kslot[p] = slot_of(base + (tid + NT * p) / (D / 8));
+    for (int p = 0; p < KPIECES; ++p) ks[p] = slot_of(base + (tid + NT * p) / (D / 8));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vslot[c] = slot_of(base + vkq * 4 + c);
+    for (int c = 0; c < 4; ++c) vs[c] = slot_of(base + vkq * 4 + c);
   };
-  auto fetch = [&](int tile, uint4(&kreg)[KPIECES], uint4(&vreg)[4]) {
+  auto fetch = [&](int tile) __attribute__((always_inline)) {
+    int nks[KPIECES], nvs[4];
+    load_slots(tile + 1, nks, nvs);
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: slot ids, then rows
 #pragma unroll
     for (int p = 0; p < KPIECES; ++p) {
       const uint32_t dg = (tid + NT * p) % (D / 8);
@@ -174,10 +196,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) vreg[c] = load16(row_addr(vbase, vslot[c], vdg * 16));
     }
-    load_slots(tile + 1);
+#pragma unroll
+    for (int p = 0; p < KPIECES; ++p) kslot[p] = nks[p];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vslot[c] = nvs[c];
   };
 
-  auto stash = [&](Smem<D> &buf, const uint4(&kreg)[KPIECES], const uint4(&vreg)[4]) {
+  auto stash = [&](Smem<D> &buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < KPIECES; ++p) {
       const int piece = tid + NT * p;
@@ -208,28 +233,35 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
     for (int x = 0; x < 16; ++x) o[db][x] = 0.f;
-  // Running max in raw score units (sm_scale > 0 keeps the order); this
-  // lane's share of the running sum (its half of the keys).
-  float m_run = kNegInf, l_lane = 0.f;
+  // Running max in raw score units (sm_scale > 0 keeps the order), the raw
+  // score above which it must move, and this lane's share of the running sum
+  // (its half of the keys).
   const float c2 = a.scale_log2;
+  const float slack_raw = kSlack / c2;
+  float m_run = kNegInf, m_thr = kNegInf, l_lane = 0.f;
   const f32x16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                            0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
 
-  // S^T of one 64-key tile (two 32-key blocks).
-  auto qk = [&](const Smem<D> &buf, f32x16_t(&sacc)[2]) {
+  // S^T of one 64-key tile (two 32-key blocks).  All fragment reads of a
+  // block are issued before its products, so the products do not wait on
+  // LDS latency one read at a time.
+  auto qk = [&](const Smem<D> &buf, f32x16_t(&sacc)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const uint16_t *krow = &buf.k[(kb * 32 + col) * KS + 8 * half];
-      sacc[kb] = mfma32(*reinterpret_cast<const uint4 *>(krow), qf[0], zero16);
+      uint4 kf[KSTEPS];
 #pragma unroll
-      for (int s = 1; s < KSTEPS; ++s)
-        sacc[kb] = mfma32(*reinterpret_cast<const uint4 *>(krow + 16 * s), qf[s], sacc[kb]);
+      for (int s = 0; s < KSTEPS; ++s) kf[s] = *reinterpret_cast<const uint4 *>(krow + 16 * s);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) sacc[kb] = mfma32(kf[s], qf[s], s == 0 ? zero16 : sacc[kb]);
     }
   };
 
   // (Mask,) online softmax of one tile's S^T, then O^T += V^T P^T.
-  auto softmax_pv = [&](int tile, f32x16_t(&sacc)[2], const Smem<D> &buf, auto masked) {
+  auto softmax_pv = [&](int tile, f32x16_t(&sacc)[2], const Smem<D> &buf,
+                        auto masked) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(masked)::value;
     if constexpr (MASK) {
       const int kbase_idx = tile * BN + 4 * half;
@@ -239,19 +271,28 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
         for (int x = 0; x < 16; ++x)
           if (kbase_idx + kb * 32 + 8 * (x >> 2) + (x & 3) >= lim) sacc[kb][x] = kNegInf;
     }
-    float tmax = kNegInf;
+    // This lane's half of the row (32 of the tile's 64 keys), as a tree.
+    float m16[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int x = 0; x < 16; ++x) m16[x] = fmaxf(sacc[0][x], sacc[1][x]);
 #pragma unroll
-      for (int x = 0; x < 16; ++x) tmax = fmaxf(tmax, sacc[kb][x]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    if (__any(m_new > m_run)) {  // rescale only when some row's max moved
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int x = 0; x < w; ++x) m16[x] = fmaxf(m16[x], m16[x + w]);
+    const float tmax = m16[0];
+    // The reference max only moves when a score exceeds it by more than
+    // 2^kSlack in weight; below that, weights up to 2^kSlack accumulate
+    // against the old reference (exact: numerator and denominator share it),
+    // so the O rescale is rare after the first tiles.  Each half of the wave
+    // tests its own keys; only a move needs the row max over both halves.
+    if (__any(tmax > m_thr)) {
+      const float m_new = fmaxf(m_run, fmaxf(tmax, __shfl_xor(tmax, 32)));
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run - m_new) * c2);
       l_lane *= alpha;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
       m_run = m_new;
+      m_thr = m_new + slack_raw;
     }
     const float mc = (m_run == kNegInf) ? 0.f : m_run * c2;
     // Per 16-key step: weights for those keys, rounded to bf16, then the PV
@@ -282,48 +323,68 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  // Pipeline, one barrier per tile: while tile n is multiplied from one LDS
-  // buffer, the register stage holding tile n+1 is staged into the other
-  // buffer and refilled with tile n+3; the other stage holds tile n+2 in
-  // flight.  Tiles every row of the workgroup sees whole run an unmasked
-  // step, the diagonal tiles a masked one (one code path per loop keeps the
-  // register allocation tight).
-  if (ntiles > 0) {
-    load_slots(0);
-    fetch(0, kregA, vregA);
-    stash(sm[0], kregA, vregA);
-    if (ntiles > 1) fetch(1, kregA, vregA);
-    if (ntiles > 2) fetch(2, kregB, vregB);
-    __syncthreads();
-  }
-  // The S^T products of tile n are issued first; the staging work for later
-  // tiles (V transpose, LDS writes, row fetches) then runs on the vector and
-  // memory units while the matrix cores work, followed by the softmax and PV
-  // products.  Staging past the last tile writes an LDS buffer no tile reads
-  // and reads clamped, valid rows: it is harmless and keeps the code
-  // straight-line for the scheduler.
-  auto step = [&](int tile, uint4(&kreg)[KPIECES], uint4(&vreg)[4], auto masked) {
-    f32x16_t sacc[2];
-    qk(sm[tile & 1], sacc);
-    stash(sm[(tile + 1) & 1], kreg, vreg);
-    fetch(tile + 3, kreg, vreg);
-    softmax_pv(tile, sacc, sm[tile & 1], masked);
-    __syncthreads();
-  };
-  const int n_free2 = n_free & ~1;
-  int tile = 0;
-  for (; tile < n_free2; tile += 2) {
-    step(tile, kregA, vregA, std::false_type{});
-    step(tile + 1, kregB, vregB, std::false_type{});
-  }
-  for (; tile + 1 < ntiles; tile += 2) {
-    step(tile, kregA, vregA, std::true_type{});
-    step(tile + 1, kregB, vregB, std::true_type{});
-  }
-  if (tile < ntiles) step(tile, kregA, vregA, std::true_type{});
+  // Prologue: tile 0 in buffer 0, tile 1 in registers.  It is unconditional
+  // (fetches past the last tile read clamped, valid rows), so every path into
+  // the tile loops has waited for the Q loads and the loops' memory waits
+  // stay exact.
+  load_slots(0, kslot, vslot);
+  fetch(0);
+  stash(sm[0]);
+  fetch(1);
+  __syncthreads();
 
-  if (!row_ok) return;
+  // Period k (between two barriers): tile k+1 goes from registers to LDS,
+  // tile k+2 is fetched.  The first group multiplies S^T(k) and then does
+  // softmax / PV of tile k; the second group first finishes tile k-1
+  // (softmax / PV) and then multiplies S^T(k).  Staging past the last tile
+  // writes a buffer no tile reads and reads clamped, valid rows.  Tiles every
+  // row of the workgroup sees whole skip the mask (separate loops keep the
+  // register allocation of each tight).  Both groups pass the same number of
+  // barriers.
+  f32x16_t sacc[2];
+  int cur = 0;   // buffer of tile k
+  int prev = 2;  // buffer of tile k-1
+  auto next_buf = [](int b) { return b == NBUF - 1 ? 0 : b + 1; };
+  if (wave < 4) {
+    auto period = [&](int k, auto masked) __attribute__((always_inline)) {
+      const int nb = next_buf(cur);
+      qk(sm[cur], sacc);
+      stash(sm[nb]);
+      fetch(k + 2);
+      softmax_pv(k, sacc, sm[cur], masked);
+      lds_barrier();
+      cur = nb;
+    };
+    int k = 0;
+    for (; k < n_free; ++k) period(k, std::false_type{});
+    for (; k < ntiles; ++k) period(k, std::true_type{});
+  } else {
+    auto period = [&](int k, auto masked) __attribute__((always_inline)) {
+      const int nb = next_buf(cur);
+      // tile k-1 < k: the mask choice made for tile k is safe for it
+      softmax_pv(k - 1, sacc, sm[prev], masked);
+      stash(sm[nb]);
+      fetch(k + 2);
+      qk(sm[cur], sacc);
+      lds_barrier();
+      prev = cur;
+      cur = nb;
+    };
+    // period 0: no earlier tile to finish
+    stash(sm[1]);
+    fetch(2);
+    qk(sm[0], sacc);
+    lds_barrier();
+    prev = 0;
+    cur = 1;
+    int k = 1;
+    for (; k < n_free; ++k) period(k, std::false_type{});
+    for (; k < ntiles; ++k) period(k, std::true_type{});
+    softmax_pv(ntiles - 1, sacc, sm[prev], std::true_type{});
+  }
+
   const float l_run = l_lane + __shfl_xor(l_lane, 32);
+  if (!row_ok) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((int64_t)(q0 + t) * a.n_heads + h) * D;
 #pragma unroll
@@ -338,9 +399,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
     }
 }
 
-}  // namespace
-
-hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, hipStream_t stream) {
+template <int D>
+hipError_t launch_d(const PrefillArgs &a, bool off32, hipStream_t stream) {
   const int64_t row_blocks = ((int64_t)a.max_q_len * a.group + BM - 1) / BM;
   if (row_blocks > INT32_MAX) return hipErrorInvalidValue;
   const int64_t blocks = row_blocks * a.n_kv_heads * a.batch;
@@ -348,22 +408,21 @@ hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, hipStream_t 
   PrefillArgs args = a;
   args.row_blocks = (int32_t)row_blocks;
   const dim3 grid((uint32_t)blocks);
+  if (off32)
+    hipLaunchKernelGGL((prefill_kernel<D, true>), grid, dim3(NT), 0, stream, args);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, false>), grid, dim3(NT), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, hipStream_t stream) {
   const uint64_t layer_bytes = (uint64_t)a.pool_size * a.n_kv_heads * head_dim * 2;
   const bool off32 = layer_bytes <= 0xffffffffull;
-  if (head_dim == 128) {
-    if (off32)
-      hipLaunchKernelGGL((prefill_kernel<128, true>), grid, dim3(NT), 0, stream, args);
-    else
-      hipLaunchKernelGGL((prefill_kernel<128, false>), grid, dim3(NT), 0, stream, args);
-  } else if (head_dim == 64) {
-    if (off32)
-      hipLaunchKernelGGL((prefill_kernel<64, true>), grid, dim3(NT), 0, stream, args);
-    else
-      hipLaunchKernelGGL((prefill_kernel<64, false>), grid, dim3(NT), 0, stream, args);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (head_dim == 128) return launch_d<128>(a, off32, stream);
+  if (head_dim == 64) return launch_d<64>(a, off32, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

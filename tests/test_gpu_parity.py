@@ -229,6 +229,30 @@ def test_prefill_small_matrix(H, Hk, d, q_lens, prefix, causal):
                  f"prefill {H}/{Hk}/{d}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_sharp_and_rising_scores(d, causal):
+    """Peaked softmax (keys scaled by 8) whose prefix keys also grow with their
+    position, so the row max keeps moving from tile to tile and often in only
+    one half of a tile's keys: exercises every rescale path."""
+    q_lens, prefix = [90, 5, 200], [700, 130, 64]
+    lens = [a + b for a, b in zip(q_lens, prefix)]
+    case = W.random_case(410 + d, lens, q_lens, n_heads=8, n_kv_heads=2, head_dim=d,
+                         dtype="bf16", k_scale=8.0)
+    say("prefill sharp/rising", d, causal)
+    t = W.make_tensors(case, device="cuda")
+    kb = t["k_buffer"][case.layer_id]
+    for b, (L, p0) in enumerate(zip(lens, prefix)):
+        row = int(case.req_pool_indices[b])
+        slots = torch.as_tensor(case.req_to_token[row, :p0].astype(np.int64), device="cuda")
+        ramp = torch.linspace(0.25, 1.5, p0, device="cuda", dtype=torch.float32)
+        kb[slots] = (kb[slots].float() * ramp[:, None, None]).to(kb.dtype)
+    hv = HostView(case, t)
+    out = gpu_prefill(case, t, causal=causal)
+    assert_close(to_np(out), hv.prefill_all(case, causal=causal), "bf16",
+                 f"prefill sharp d{d}")
+
+
 def test_prefill_full_config_sampled():
     case = W.ragged_prefill()
     say("ragged prefill full")

@@ -202,3 +202,7 @@ def test_argument_errors_before_launch(lib):
                                  None) == B.PKV_ERR_DTYPE
     assert lib.pkv_paged_prefill(C.byref(p), 0, C.byref(sp), fake, 4, 0.1, 1, fake,
                                  None) == B.PKV_ERR_NULL
+    # prefill ranks raw scores, so the scale must be positive
+    for bad_scale in (0.0, -0.1, float("inf")):
+        assert lib.pkv_paged_prefill(C.byref(p), 0, C.byref(sp), fake, 4, bad_scale, 1, fake,
+                                     None) == B.PKV_ERR_SHAPE
