@@ -271,15 +271,20 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
         for (int x = 0; x < 16; ++x)
           if (kbase_idx + kb * 32 + 8 * (x >> 2) + (x & 3) >= lim) sacc[kb][x] = kNegInf;
     }
-    // This lane's half of the row (32 of the tile's 64 keys), as a tree.
-    float m16[16];
+    // Max over this lane's half of the row (32 of the tile's 64 keys): a
+    // tree of three-input maxes, 17 instructions at depth 4.
+    auto max3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
+    float m11[11];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) m16[x] = fmaxf(sacc[0][x], sacc[1][x]);
-#pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-      for (int x = 0; x < w; ++x) m16[x] = fmaxf(m16[x], m16[x + w]);
-    const float tmax = m16[0];
+    for (int j = 0; j < 10; ++j) {
+      const int e = 3 * j;
+      m11[j] = max3(sacc[e >> 4][e & 15], sacc[(e + 1) >> 4][(e + 1) & 15],
+                    sacc[(e + 2) >> 4][(e + 2) & 15]);
+    }
+    m11[10] = fmaxf(sacc[1][14], sacc[1][15]);
+    const float tmax = fmaxf(max3(max3(m11[0], m11[1], m11[2]), max3(m11[3], m11[4], m11[5]),
+                                  max3(m11[6], m11[7], m11[8])),
+                             fmaxf(m11[9], m11[10]));
     // The reference max only moves when a score exceeds it by more than
     // 2^kSlack in weight; below that, weights up to 2^kSlack accumulate
     // against the old reference (exact: numerator and denominator share it),
