@@ -15,7 +15,8 @@
 // Keys stream through LDS in tiles of 64, gathered by slot:
 //   S^T (keys x rows) = K Q^T : v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
 //                               B = the wave's Q rows held in registers;
-//   O^T (dims x rows) += V^T P^T : A = V^T from LDS (V is stored transposed),
+//   O^T (dims x rows) += V^T P^T : A = V^T, read from the V rows in LDS with
+//                               transposing LDS reads (ds_read_b64_tr_b16),
 //                               B = the softmax weights, rounded to bf16,
 //                               taken straight from the S^T accumulators.
 // With S^T in this orientation every lane holds one query row, so the
@@ -66,19 +67,25 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Position of key k of a 64-key tile inside a transposed V row: bits 2 and 3 of
-// the key index are swapped, so that the eight keys one lane feeds to a PV
-// product (keys 16t + {0..3, 8..11} or 16t + {4..7, 12..15}) are contiguous.
-__device__ __forceinline__ int vpos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane j supplies the address
+// of 4 consecutive 16-bit elements (row j of a 16 x 4 block M); lane l then
+// receives M[l/4 + 4r][l%4] for r = 0..3.  With row j = (key j/4, dims
+// 4(j%4) .. +3) of a [key][dim] tile, lane l receives dim l of 4 consecutive
+// keys: the V^T operand read straight from V rows.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p);
+  return __builtin_bit_cast(uint2, v);
 }
 
 template <int D>
 struct Smem {
   static constexpr int KS = D + 8;   // K row stride (elements), 16-byte pad
-  static constexpr int VS = BN + 8;  // V^T row stride (elements), 16-byte pad
+  static constexpr int VS = D + 32;  // V row stride (elements), 64-byte pad
   uint16_t k[BN * KS];
-  uint16_t vt[D * VS];
+  uint16_t v[BN * VS];
 };
 
 // OFF32: every row of the layer lies within 4 GiB of the layer base, so row
@@ -89,9 +96,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   constexpr int VS = Smem<D>::VS;
   constexpr int KSTEPS = D / 16;             // MFMA steps over head_dim for S^T
   constexpr int DBLK = D / 32;               // 32-dim blocks of O^T
-  constexpr int KPIECES = BN * D / 8 / NT;   // 16-byte K pieces per thread per tile
-  constexpr int VJOBS = (BN / 4) * (D / 8);  // (4-key, 8-dim) V jobs per tile
-  static_assert(KPIECES >= 1 && VJOBS % 64 == 0 && VJOBS <= NT / 2, "staging split");
+  constexpr int KPIECES = BN * D / 8 / NT;   // 16-byte K (and V) pieces per thread per tile
+  static_assert(KPIECES >= 1, "staging split");
   __shared__ Smem<D> sm[NBUF];
 
   // Workgroups are dispatched to the 8 XCDs round-robin by linear id; taking
@@ -158,15 +164,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
       return base + ((int64_t)slot * row_bytes + col_bytes);
   };
 
-  // Global -> register staging of one tile.  K: every thread, 16 lanes per
-  // key row.  V: the first VJOBS threads (all in the first group: its
-  // staging sits in its matrix phase), lanes first running over the 16 key
-  // quads of the tile so that the transposed LDS writes of a 16-lane group
-  // fill 128 distinct bytes.
-  uint4 kreg[KPIECES], vreg[4];
-  const int vkq = tid & 15;  // keys 4 * vkq .. + 3
-  const int vdg = tid >> 4;  // dims 8 * vdg .. + 7
-  const bool vjob = wave < VJOBS / 64;
+  // Global -> register staging of one tile: every thread copies KPIECES
+  // 16-byte pieces of K and the same pieces of V (16 lanes per key row), so
+  // one slot id serves both.
+  uint4 kreg[KPIECES], vreg[KPIECES];
 
   // Slot ids are loaded one tile ahead of the rows they address, so a
   // tile's K/V loads never wait on a table load.  They are issued before the
@@ -174,32 +175,25 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   // the next fetch's wait for its slot ids leaves these rows in flight.  Keys
   // past kv_end read the last valid key instead (always masked), keeping
   // every load unconditional.
-  int kslot[KPIECES], vslot[4];
+  int slot[KPIECES];
   auto slot_of = [&](int j) { return table[(uint32_t)min(j, kv_end - 1)]; };
-  auto load_slots = [&](int tile, int(&ks)[KPIECES], int(&vs)[4]) {
+  auto load_slots = [&](int tile, int(&ks)[KPIECES]) {
     const int base = tile * BN;
 #pragma unroll
     for (int p = 0; p < KPIECES; ++p) ks[p] = slot_of(base + (tid + NT * p) / (D / 8));
-#pragma unroll
-    for (int c = 0; c < 4; ++c) vs[c] = slot_of(base + vkq * 4 + c);
   };
   auto fetch = [&](int tile) __attribute__((always_inline)) {
-    int nks[KPIECES], nvs[4];
-    load_slots(tile + 1, nks, nvs);
+    int ns[KPIECES];
+    load_slots(tile + 1, ns);
     __builtin_amdgcn_sched_barrier(0);  // keep the issue order: slot ids, then rows
 #pragma unroll
     for (int p = 0; p < KPIECES; ++p) {
       const uint32_t dg = (tid + NT * p) % (D / 8);
-      kreg[p] = load16(row_addr(kbase, kslot[p], dg * 16));
-    }
-    if (vjob) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) vreg[c] = load16(row_addr(vbase, vslot[c], vdg * 16));
+      kreg[p] = load16(row_addr(kbase, slot[p], dg * 16));
+      vreg[p] = load16(row_addr(vbase, slot[p], dg * 16));
     }
 #pragma unroll
-    for (int p = 0; p < KPIECES; ++p) kslot[p] = nks[p];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) vslot[c] = nvs[c];
+    for (int p = 0; p < KPIECES; ++p) slot[p] = ns[p];
   };
 
   auto stash = [&](Smem<D> &buf) __attribute__((always_inline)) {
@@ -209,22 +203,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
       const int key = piece / (D / 8);
       const int dg = piece - key * (D / 8);
       store16(&buf.k[key * KS + dg * 8], kreg[p]);
-    }
-    if (vjob) {
-      // Transpose 4 keys x 8 dims: each dim becomes 4 contiguous keys.
-      const int pos = vpos(vkq * 4);
-      const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
-                                {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
-                                {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
-                                {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        uint2 v;
-        v.x = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
-        v.y = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
-        *reinterpret_cast<uint2 *>(&buf.vt[(vdg * 8 + e) * VS + pos]) = v;
-      }
+      store16(&buf.v[key * VS + dg * 8], vreg[p]);
     }
   };
 
@@ -236,6 +215,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   // Running max in raw score units (sm_scale > 0 keeps the order), the raw
   // score above which it must move, and this lane's share of the running sum
   // (its half of the keys).
+  // Transposed V reads: lane l of 16-lane group g addresses key (l%16)/4 of
+  // its 4-key run, dims 16(g&1) + 4(l%4) .. +3 of the 32-dim block.
+  const int gl = lane & 15;
+  const int voff = 16 * ((lane >> 4) & 1) + 4 * (gl & 3);
   const float c2 = a.scale_log2;
   const float slack_raw = kSlack / c2;
   float m_run = kNegInf, m_thr = kNegInf, l_lane = 0.f;
@@ -321,9 +304,12 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
       l_lane = dot2_bf16(pf.w, kOnes, l_lane);
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        const uint4 vf =
-            *reinterpret_cast<const uint4 *>(&buf.vt[(db * 32 + col) * VS + 16 * ts + 8 * half]);
-        o[db] = mfma32(vf, pf, o[db]);
+        // V^T operand: keys 16ts + 4half + {0..3} and 16ts + 8 + 4half + {0..3}
+        // (the keys this lane's weights cover), dim db*32 + lane % 32.
+        const uint16_t *vb = &buf.v[(16 * ts + 4 * half + (gl >> 2)) * VS + db * 32 + voff];
+        const uint2 lo = lds_read_tr16(vb);
+        const uint2 hi = lds_read_tr16(vb + 8 * VS);
+        o[db] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf, o[db]);
       }
     }
   };
@@ -332,7 +318,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   // (fetches past the last tile read clamped, valid rows), so every path into
   // the tile loops has waited for the Q loads and the loops' memory waits
   // stay exact.
-  load_slots(0, kslot, vslot);
+  load_slots(0, slot);
   fetch(0);
   stash(sm[0]);
   fetch(1);
