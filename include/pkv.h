@@ -210,6 +210,49 @@ pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_d
                                   void *stream /* hipStream_t */);
 
 /* ------------------------------------------------------------------------
+ * One decode step in one launch ("Inference" guide, section "KVCache System":
+ * the new token's K/V are written at out_cache_loc; section "Attention
+ * Backend": decode then attends the paged cache; commit history of
+ * tests/inference/test_cache.py: split partials in a caller-owned workspace
+ * merged by log-sum-exp).  Computes exactly what pkv_kv_store (of the step's
+ * batch new tokens) followed by pkv_paged_decode and pkv_paged_decode_merge
+ * computes, for decode steps (one new token per request: step->n_new ==
+ * batch, qo_indptr unused):
+ *   k_buffer[layer, out_cache_loc[b]] = k_new[b] (same for v), then
+ *   out[b, h] = sum_j softmax_j(q[b,h] . k_j * sm_scale) v_j over the
+ *   seq_lens[b] keys of request b, the new one included.
+ * k_new / v_new: device [batch, n_kv_heads, head_dim], pool dtype.  q, out:
+ * device [batch, n_heads, head_dim], pool dtype.
+ * For bf16 pools with head_dim 128 this is one kernel: each split is taken by
+ * a four-wave workgroup, the new token's rows are read from k_new / v_new
+ * (and written to the pool by one workgroup), and the last workgroup of each
+ * (request, kv-head) to finish merges that kv-head's heads.  Requirements of
+ * that path: out_cache_loc[b] is the slot of position seq_lens[b] - 1 of
+ * request b and no other position read in this step maps to it (fresh slots,
+ * as pkv_validate_step checks for duplicates); sync points to sync_len >=
+ * batch * n_heads int32 counters that are zero before the first call (each
+ * call leaves them zero; re-zero them after a failed call).  Other shapes run
+ * the three launches (sync unused).
+ * workspace: pkv_decode_workspace_bytes(batch, n_heads, head_dim, num_splits)
+ * bytes, layout as for pkv_paged_decode.  num_splits: see
+ * pkv_decode_step_pick_splits.
+ * Errors: as pkv_paged_decode, plus PKV_ERR_NULL for missing k_new / v_new /
+ * out / sync / out_cache_loc and PKV_ERR_SHAPE for n_new != batch or a short
+ * sync buffer.
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_paged_decode_step(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,
+                                 const void *q, const void *k_new, const void *v_new,
+                                 int32_t n_heads, float sm_scale, int32_t num_splits,
+                                 void *workspace, size_t ws_bytes, int32_t *sync,
+                                 int64_t sync_len, void *out, void *stream /* hipStream_t */);
+
+/* Host-only split count for pkv_paged_decode_step: the single-wave choice of
+ * pkv_decode_pick_splits divided by four (each split of the fused step is
+ * taken by four wavefronts), clamped to [1, max_splits]. */
+int32_t pkv_decode_step_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_heads,
+                                    int32_t max_len, int64_t total_len, int32_t max_splits);
+
+/* ------------------------------------------------------------------------
  * Ragged paged prefill ("Inference" guide, section "Attention Backend": after
  * the K/V write, a ragged-batch kernel reads K/V straight from the flat pool
  * through req_to_token, with each request's query and key counts taken from

@@ -70,6 +70,33 @@ def decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceSte
     return out
 
 
+def decode_sync(batch: int, n_heads: int, device="cuda"):
+    """Ticket counters of the fused decode step (zero; every call leaves them zero)."""
+    import torch
+    return torch.zeros(batch * n_heads, dtype=torch.int32, device=device)
+
+
+def fused_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q,
+                      k_new, v_new, sm_scale: float, num_splits: Optional[int] = None,
+                      workspace=None, sync=None, out=None):
+    """The decode step (K/V write, split attention, merge) in one library call:
+    one launch for bf16 pools with head_dim 128.  Returns out."""
+    import torch
+    H, d = int(q.shape[1]), int(q.shape[2])
+    if num_splits is None:
+        num_splits = B.pkv_decode_step_pick_splits(step.batch, int(k_buffer.shape[2]), H,
+                                                   step.max_len, step.total_len)
+    if workspace is None:
+        workspace = decode_workspace(step.batch, H, d, num_splits, q.device)
+    if sync is None:
+        sync = decode_sync(step.batch, H, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    B.pkv_paged_decode_step(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, k_new, v_new,
+                            sm_scale, num_splits, workspace, sync, out)
+    return out
+
+
 def prefill_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q, k_new,
                  v_new, sm_scale: float, causal: bool = True, out=None, write_kv: bool = True):
     """K/V write of the step's new tokens, then ragged paged prefill."""

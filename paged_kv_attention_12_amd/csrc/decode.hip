@@ -355,43 +355,31 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, const 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs a) {
+constexpr int kMfmaD = 128;  // head_dim of the matrix-core path
+constexpr int kKT = 32;      // keys per iteration of a wavefront
+
+// Online-softmax attention of one wavefront over the keys [start, end) of
+// request b, for the query heads h0 .. h0 + 15 of kv-head hk (columns c with
+// col_ok; the others are zero).  The workgroup stages the slot ids of up to
+// kSlotTile keys at a time in LDS (all four waves take part in the barriers);
+// within each staged run the wavefront takes the 32-key tiles first,
+// first + TS, first + 2 TS, ...  With NEW the key at position newpos is read
+// from the rows knew / vnew (this kv-head's K and V of the token written in
+// the same step) instead of the pool.  On return o[e][i] holds the
+// unnormalised O[head c][32g + 8i + e] against the base-2 running max m_run,
+// and l_tot the running sum (both per head, equal in the four lane groups).
+template <int TS, bool NEW>
+__device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot, int b,
+                                            int start, int end, int first, bool active, int hk,
+                                            int h0, bool col_ok, const uint16_t *knew,
+                                            const uint16_t *vnew, int newpos, f32x4_t (&o)[8],
+                                            float &m_run, float &l_tot) {
   constexpr int P = 2;  // register tile sets (deeper rings measured no faster)
-  constexpr int D = 128;
-  constexpr int KT = 32;  // keys per iteration
-  __shared__ int32_t s_slot[kSlotTile];
-
-  const int b = blockIdx.z;
-  const int s = blockIdx.y;
-  const int L = a.seq_lens[b];
-  const int start = s * a.chunk;
-  const int end = min(L, start + a.chunk);
-
+  constexpr int D = kMfmaD;
+  constexpr int KT = kKT;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int g = lane >> 4;
-  const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const bool active = task < a.n_kv_heads * a.n_chunks;
-  const int hk = active ? task / a.n_chunks : 0;
-  const int g0 = active ? (task - hk * a.n_chunks) * a.heads_per_chunk : 0;
-  const int ng = active ? min(a.heads_per_chunk, a.group - g0) : 0;
-  const int h0 = hk * a.group + g0;
-  const bool col_ok = c < ng;
-  const int S = a.num_splits;
-  const int64_t pr = ((int64_t)b * a.n_heads + h0 + c) * S + s;  // partial row of head h0 + c
-
-  if (start >= end) {
-    if (active && col_ok) {
-      float4 *o = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) o[x] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (g == 0) {
-        a.ml_part[pr * 2 + 0] = kNegInf;
-        a.ml_part[pr * 2 + 1] = 0.f;
-      }
-    }
-    return;
-  }
 
   // Q^T operand: head c, dims 8g + 32k .. +8 for step k.
   uint4 qf[4];
@@ -407,12 +395,13 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs
   const int64_t row_elems = (int64_t)a.n_kv_heads * D;
   const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k_layer) + (int64_t)hk * D + 8 * g;
   const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v_layer) + (int64_t)hk * D + 8 * c;
+  const uint16_t *knew_l = NEW ? knew + 8 * g : nullptr;
+  const uint16_t *vnew_l = NEW ? vnew + 8 * c : nullptr;
 
-  f32x4_t o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf;  // base-2 running max of head c (same in all four groups)
-  float l_lane = 0.f;     // this lane's share of the running sum
+  m_run = kNegInf;     // base-2 running max of head c (same in all four groups)
+  float l_lane = 0.f;  // this lane's share of the running sum
 
   // K rows: keys 16t + c (t < 2), 16 bytes at dims 8g + 32k.  V rows: keys
   // 4g + i and 16 + 4g + i (i < 4), dims 8c .. 8c + 7.  Tokens past the end
@@ -422,17 +411,24 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs
   auto fetch = [&](uint4(&kx)[2][4], uint4(&vx)[8], int j0, int r0, int r1) {
     const int last = r1 - 1 - r0;
     const int jb = j0 - r0;
-    int sk[2], sv[8];
+    int jk[2], jv[8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) sk[t] = s_slot[min(jb + 16 * t + c, last)];
+    for (int t = 0; t < 2; ++t) jk[t] = min(jb + 16 * t + c, last);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) sv[x] = s_slot[min(jb + 16 * (x >> 2) + 4 * g + (x & 3), last)];
+    for (int x = 0; x < 8; ++x) jv[x] = min(jb + 16 * (x >> 2) + 4 * g + (x & 3), last);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t *kp = kbase + (int64_t)s_slot[jk[t]] * row_elems;
+      if constexpr (NEW) kp = (r0 + jk[t] == newpos) ? knew_l : kp;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) kx[t][k] = load16(kbase + (int64_t)sk[t] * row_elems + 32 * k);
+      for (int k = 0; k < 4; ++k) kx[t][k] = load16(kp + 32 * k);
+    }
 #pragma unroll
-    for (int x = 0; x < 8; ++x) vx[x] = load16(vbase + (int64_t)sv[x] * row_elems);
+    for (int x = 0; x < 8; ++x) {
+      const uint16_t *vp = vbase + (int64_t)s_slot[jv[x]] * row_elems;
+      if constexpr (NEW) vp = (r0 + jv[x] == newpos) ? vnew_l : vp;
+      vx[x] = load16(vp);
+    }
   };
 
   auto process = [&](const uint4(&kx)[2][4], const uint4(&vx)[8], int j0, int r1) {
@@ -500,29 +496,86 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs
   for (int r0 = start; r0 < end; r0 += kSlotTile) {
     const int r1 = min(end, r0 + kSlotTile);
     if (r0 != start) __syncthreads();
-    for (int j = r0 + (int)threadIdx.x; j < r1; j += 256) s_slot[j - r0] = table[j];
+    {
+      // all of this thread's slot-id loads first, then the LDS stores: one
+      // memory round trip per staged run
+      constexpr int SPT = kSlotTile / 256;
+      int v[SPT];
+#pragma unroll
+      for (int k = 0; k < SPT; ++k) {
+        const int j = r0 + (int)threadIdx.x + 256 * k;
+        v[k] = j < r1 ? table[j] : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < SPT; ++k) {
+        const int j = r0 + (int)threadIdx.x + 256 * k;
+        if (j < r1) s_slot[j - r0] = v[k];
+      }
+    }
     __syncthreads();
     if (!active) continue;
-    const int ntiles = (r1 - r0 + KT - 1) / KT;
+    const int round_tiles = (r1 - r0 + KT - 1) / KT;
+    const int ntiles = first < round_tiles ? (round_tiles - first + TS - 1) / TS : 0;
+    auto j0_of = [&](int i) { return r0 + (first + i * TS) * KT; };
 #pragma unroll
-    for (int q = 0; q < P - 1; ++q) fetch(kr[q], vr[q], r0 + q * KT, r0, r1);
+    for (int q = 0; q < P - 1; ++q) fetch(kr[q], vr[q], j0_of(q), r0, r1);
     int i = 0;
     for (; i + P <= ntiles; i += P) {
 #pragma unroll
       for (int q = 0; q < P; ++q) {
-        fetch(kr[(q + P - 1) % P], vr[(q + P - 1) % P], r0 + (i + q + P - 1) * KT, r0, r1);
-        process(kr[q], vr[q], r0 + (i + q) * KT, r1);
+        fetch(kr[(q + P - 1) % P], vr[(q + P - 1) % P], j0_of(i + q + P - 1), r0, r1);
+        process(kr[q], vr[q], j0_of(i + q), r1);
       }
     }
 #pragma unroll
     for (int q = 0; q < P - 1; ++q)
-      if (i + q < ntiles) process(kr[q], vr[q], r0 + (i + q) * KT, r1);
+      if (i + q < ntiles) process(kr[q], vr[q], j0_of(i + q), r1);
   }
-  if (!active) return;
-
-  float l_tot = l_lane + __shfl_xor(l_lane, 16);
+  l_tot = l_lane + __shfl_xor(l_lane, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (!col_ok) return;
+}
+
+__global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs a) {
+  constexpr int D = kMfmaD;
+  __shared__ int32_t s_slot[kSlotTile];
+
+  const int b = blockIdx.z;
+  const int s = blockIdx.y;
+  const int L = a.seq_lens[b];
+  const int start = s * a.chunk;
+  const int end = min(L, start + a.chunk);
+
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const bool active = task < a.n_kv_heads * a.n_chunks;
+  const int hk = active ? task / a.n_chunks : 0;
+  const int g0 = active ? (task - hk * a.n_chunks) * a.heads_per_chunk : 0;
+  const int ng = active ? min(a.heads_per_chunk, a.group - g0) : 0;
+  const int h0 = hk * a.group + g0;
+  const bool col_ok = c < ng;
+  const int S = a.num_splits;
+  const int64_t pr = ((int64_t)b * a.n_heads + h0 + c) * S + s;  // partial row of head h0 + c
+
+  if (start >= end) {
+    if (active && col_ok) {
+      float4 *o = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) o[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (g == 0) {
+        a.ml_part[pr * 2 + 0] = kNegInf;
+        a.ml_part[pr * 2 + 1] = 0.f;
+      }
+    }
+    return;
+  }
+
+  f32x4_t o[8];
+  float m_run, l_tot;
+  attend_mfma<1, false>(a, s_slot, b, start, end, 0, active, hk, h0, col_ok, nullptr, nullptr, -1,
+                        o, m_run, l_tot);
+  if (!active || !col_ok) return;
   // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
   const float inv = 1.f / l_tot;
   float4 *op = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
@@ -535,6 +588,200 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs
     a.ml_part[pr * 2 + 0] = m_run;
     a.ml_part[pr * 2 + 1] = l_tot;
   }
+}
+
+// ---------------------------------------------------------------------------
+// One decode step in one launch (bf16, head_dim 128): the K/V write of every
+// request's new token, the split attention and the merge (the three steps of
+// the "KVCache System" write plus the "Attention Backend" decode call).
+// A workgroup owns (request b, task = kv-head and chunk of <= 16 of its query
+// heads, split s); its four waves take interleaved 32-key tiles of the split
+// and combine their (m, l, o) states in LDS into one split partial, written
+// in the workspace format of the split kernel.  The new token's K/V rows are
+// read from k_new / v_new (the workgroup of the split holding the token also
+// writes them to the pool; nothing in this launch reads that pool row).  Each
+// workgroup then takes a ticket on the (b, task) counter in sync; the last of
+// the num_splits workgroups merges the task's partials into out and resets
+// the counter to zero.
+// Relaxed device-scope (agent) accesses: coherent across the XCDs' L2s
+// without the whole-cache write-back and invalidate of a device fence.
+__device__ __forceinline__ void store_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15): wait for this wave's vector
+// memory operations only.
+constexpr int kWaitVmem0 = 0x0F70;
+
+__global__ void __launch_bounds__(256, 2) decode_step_kernel(const StepArgs sa) {
+  constexpr int D = kMfmaD;
+  const DecodeArgs &a = sa.d;
+  // LDS: slot ids while attending, then the four waves' states.
+  __shared__ __align__(16) char s_raw[4 * 16 * D * 4 + 2 * 4 * 16 * 4];
+  __shared__ int s_last;
+  int32_t *s_slot = reinterpret_cast<int32_t *>(s_raw);
+  static_assert(kSlotTile * 4 <= 4 * 16 * D * 4, "LDS reuse");
+  float *s_o = reinterpret_cast<float *>(s_raw);       // [wave][head][dim]
+  float *s_m = s_o + 4 * 16 * D;                       // [wave][head]
+  float *s_l = s_m + 4 * 16;                           // [wave][head]
+
+  const int b = blockIdx.z;
+  const int s = blockIdx.y;
+  const int task = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  const int L = a.seq_lens[b];
+  const int start = s * a.chunk;
+  const int end = min(L, start + a.chunk);
+  const int hk = task / a.n_chunks;
+  const int chunk_i = task - hk * a.n_chunks;
+  const int g0 = chunk_i * a.heads_per_chunk;
+  const int ng = min(a.heads_per_chunk, a.group - g0);
+  const int h0 = hk * a.group + g0;
+  const int S = a.num_splits;
+  const int newpos = L - 1;
+  const int64_t new_row = ((int64_t)b * a.n_kv_heads + hk) * D;  // element offset in k_new / v_new
+  const uint16_t *knew = reinterpret_cast<const uint16_t *>(sa.k_new) + new_row;
+  const uint16_t *vnew = reinterpret_cast<const uint16_t *>(sa.v_new) + new_row;
+
+  // The pool write of the new token's row of this kv-head (once per kv-head).
+  if (chunk_i == 0 && start <= newpos && newpos < end && tid < 2 * D / 8) {
+    const int64_t loc = sa.out_cache_loc[b];
+    const int64_t dst = (loc * a.n_kv_heads + hk) * D + 8 * (tid & 15);
+    if (tid < D / 8)
+      store16(reinterpret_cast<uint16_t *>(sa.k_layer_w) + dst, load16(knew + 8 * (tid & 15)));
+    else
+      store16(reinterpret_cast<uint16_t *>(sa.v_layer_w) + dst, load16(vnew + 8 * (tid & 15)));
+  }
+
+  f32x4_t o[8];
+  float m_run, l_tot;
+  attend_mfma<4, true>(a, s_slot, b, start, end, wave, true, hk, h0, c < ng, knew, vnew, newpos, o,
+                       m_run, l_tot);
+
+  // Combine the four waves' states into the split partial.
+  __syncthreads();  // slot ids are dead
+  if (c < ng) {
+    float *wo = s_o + (wave * 16 + c) * D + 32 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<float4 *>(wo + 8 * i) = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
+      *reinterpret_cast<float4 *>(wo + 8 * i + 4) = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
+    }
+    if (g == 0) {
+      s_m[wave * 16 + c] = m_run;
+      s_l[wave * 16 + c] = l_tot;
+    }
+  }
+  __syncthreads();
+  {
+    const int hc = tid >> 4;        // head column
+    const int d0 = (tid & 15) * 8;  // 8 dims
+    if (hc < ng) {
+      float mw[4], lw[4];
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        mw[w] = s_m[w * 16 + hc];
+        lw[w] = s_l[w * 16 + hc];
+        if (lw[w] > 0.f) M = fmaxf(M, mw[w]);
+      }
+      float f[4], lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        f[w] = lw[w] > 0.f ? fast_exp2(mw[w] - M) : 0.f;
+        lsum = fmaf(f[w], lw[w], lsum);
+      }
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (f[w] == 0.f) continue;  // an empty wave's o is never read
+        const float *wo = s_o + (w * 16 + hc) * D + d0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(f[w], wo[e], acc[e]);
+      }
+      // Device-scope stores: the partial is read by whichever workgroup (on
+      // any XCD) merges, so it must not wait in this XCD's L2.
+      const int64_t pr = ((int64_t)b * a.n_heads + h0 + hc) * S + s;
+      float *op = a.o_part + pr * D + d0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) store_agent(op + e, acc[e] * inv);
+      if ((tid & 15) == 0) {
+        store_agent(a.ml_part + pr * 2 + 0, lsum > 0.f ? M : kNegInf);
+        store_agent(a.ml_part + pr * 2 + 1, lsum);
+      }
+    }
+  }
+
+  // Ticket: the last split of (b, task) to finish merges.  Release: every
+  // thread's device-scope partial stores have completed (vmcnt 0) before the
+  // barrier, and the barrier before the ticket.  The partials are the only
+  // data another workgroup reads, so no L2 write-back is needed.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+  __syncthreads();
+  if (tid == 0) {
+    const int t = __hip_atomic_fetch_add(&sa.sync[(int64_t)b * sa.tasks + task], 1,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = t == S - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+  // Merge: wave w takes heads w, w + 4, ...; lane l dims 2l, 2l + 1.  Up to
+  // 32 splits per memory round trip.
+  constexpr int KB = 32;
+  for (int hc = wave; hc < ng; hc += 4) {
+    const int64_t row = (int64_t)b * a.n_heads + h0 + hc;
+    const float *ml = a.ml_part + row * S * 2;
+    const float *op = a.o_part + row * S * D + 2 * lane;
+    float M = kNegInf, den = 0.f, n0 = 0.f, n1 = 0.f;
+    for (int s0 = 0; s0 < S; s0 += KB) {
+      float mv[KB], lv[KB];
+      float2 ov[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int sk = min(s0 + k, S - 1);
+        mv[k] = load_agent(ml + 2 * sk);
+        lv[k] = s0 + k < S ? load_agent(ml + 2 * sk + 1) : 0.f;
+        ov[k] = make_float2(load_agent(op + (int64_t)sk * D), load_agent(op + (int64_t)sk * D + 1));
+      }
+      float bm = M;
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+        if (lv[k] > 0.f) bm = fmaxf(bm, mv[k]);
+      if (bm != M && M != kNegInf) {  // earlier batches were weighed against M
+        const float f = fast_exp2(M - bm);
+        den *= f;
+        n0 *= f;
+        n1 *= f;
+      }
+      M = bm;
+      const float Mr = (M == kNegInf) ? 0.f : M;
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const float w = lv[k] > 0.f ? lv[k] * fast_exp2(mv[k] - Mr) : 0.f;
+        den += w;
+        n0 = fmaf(w, ov[k].x, n0);
+        n1 = fmaf(w, ov[k].y, n1);
+      }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(sa.out) + row * D + 2 * lane) =
+        pack_bf16x2(n0 * inv, n1 * inv);
+  }
+  if (tid == 0)
+    __hip_atomic_store(&sa.sync[(int64_t)b * sa.tasks + task], 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int D>
@@ -585,6 +832,17 @@ hipError_t launch_paged_decode(const DecodeArgs &args, int dtype, int head_dim,
     if (head_dim == 64) return decode_dispatch_ng<float, 64>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_step(const StepArgs &args, hipStream_t stream) {
+  StepArgs sa = args;
+  DecodeArgs &a = sa.d;
+  a.n_chunks = (a.group + 15) / 16;
+  a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
+  sa.tasks = a.n_kv_heads * a.n_chunks;
+  const dim3 grid(sa.tasks, a.num_splits, a.batch);
+  hipLaunchKernelGGL(decode_step_kernel, grid, dim3(256), 0, stream, sa);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_merge(const MergeArgs &a, int dtype, int head_dim, hipStream_t stream) {

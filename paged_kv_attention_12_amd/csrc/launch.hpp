@@ -42,6 +42,21 @@ struct DecodeArgs {
 // dtype: 0 = f32, 1 = bf16
 hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
 
+// One fused decode step (bf16, head_dim 128): new-token K/V write, split
+// attention and merge in one launch.
+struct StepArgs {
+  DecodeArgs d;               // o_part / ml_part: the decode workspace
+  const void *k_new;          // [batch, n_kv_heads, head_dim]
+  const void *v_new;
+  void *k_layer_w;            // d.k_layer, writable
+  void *v_layer_w;
+  const int32_t *out_cache_loc;  // [batch]
+  int32_t *sync;              // [batch * tasks] ticket counters, zero between calls
+  void *out;                  // [batch, n_heads, head_dim] bf16
+  int32_t tasks;              // kv-heads x head chunks (set by the launcher)
+};
+hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream);
+
 struct MergeArgs {
   const float *o_part;
   const float *ml_part;

@@ -206,3 +206,40 @@ def test_argument_errors_before_launch(lib):
     for bad_scale in (0.0, -0.1, float("inf")):
         assert lib.pkv_paged_prefill(C.byref(p), 0, C.byref(sp), fake, 4, bad_scale, 1, fake,
                                      None) == B.PKV_ERR_SHAPE
+
+
+def test_fused_step_split_choice(lib):
+    # a quarter of the single-wave choice (four waves share a split), at least 1
+    for args in [(1, 8, 32, 1024, 1024), (1, 8, 32, 32768, 32768), (8, 8, 64, 131072, 8 * 131072),
+                 (64, 8, 32, 8192, 266000), (2, 2, 4, 17, 22)]:
+        s1 = B.pkv_decode_pick_splits(*args, max_splits=65535)
+        assert B.pkv_decode_step_pick_splits(*args) == max(1, (s1 + 3) // 4)
+    assert B.pkv_decode_step_pick_splits(1, 8, 32, 32768, 32768) == 32
+    assert B.pkv_decode_step_pick_splits(1, 8, 32, 32768, 32768, max_splits=5) == 5
+
+
+def test_fused_step_argument_errors(lib):
+    """Host checks of pkv_paged_decode_step; nothing reaches the device."""
+    p = _fake_pool()
+    s = B.pkv_step()
+    s.batch, s.req_pool_indices, s.seq_lens, s.max_len = 2, 0x10, 0x20, 8
+    s.out_cache_loc, s.n_new = 0x30, 2
+    fake = C.c_void_p(0x4000)
+    sync = C.c_void_p(0x5000)
+    need = lib.pkv_decode_workspace_bytes(2, 4, 128, 4)
+    call = lambda step=s, pool=p, sync_ptr=sync, sync_len=8, ws=need, ns=4: \
+        lib.pkv_paged_decode_step(C.byref(pool), 0, C.byref(step), fake, fake, fake, 4, 0.1, ns,
+                                  fake, ws, sync_ptr, sync_len, fake, None)
+    assert call(sync_ptr=None) == B.PKV_ERR_NULL
+    assert call(sync_len=7) == B.PKV_ERR_SHAPE          # needs batch * n_heads counters
+    assert call(ws=need - 1) == B.PKV_ERR_WORKSPACE_TOO_SMALL
+    assert call(ns=0) == B.PKV_ERR_SHAPE
+    s3 = B.pkv_step()
+    s3.batch, s3.req_pool_indices, s3.seq_lens, s3.max_len = 2, 0x10, 0x20, 8
+    s3.out_cache_loc, s3.n_new = 0x30, 3                  # not one new token per request
+    assert call(step=s3) == B.PKV_ERR_SHAPE
+    s0 = B.pkv_step()
+    s0.batch, s0.req_pool_indices, s0.seq_lens, s0.max_len = 2, 0x10, 0x20, 8
+    s0.n_new = 2                                          # no out_cache_loc
+    assert call(step=s0) == B.PKV_ERR_NULL
+    assert call(pool=_fake_pool(head_dim=96)) == B.PKV_ERR_UNSUPPORTED
