@@ -109,6 +109,29 @@ class DecodeRunner:
         self.decode(layer, st)
         self.merge(st)
 
+
+class FusedDecodeRunner(DecodeRunner):
+    """The same workload stepped through pkv_paged_decode_step: one launch for
+    the K/V write, the split attention and the merge."""
+
+    def __init__(self, case, fill_all_layers=True, num_splits=None):
+        from paged_kv_attention_12_amd import api, binding as B
+        super().__init__(case, fill_all_layers)
+        c = self.case
+        self.num_splits = num_splits or B.pkv_decode_step_pick_splits(
+            c.batch, c.n_kv_heads, c.n_heads, self.step.max_len, self.step.total_len)
+        self.ws = api.decode_workspace(c.batch, c.n_heads, c.head_dim, self.num_splits)
+        self.ws_bytes = self.ws.numel() * 4
+        self.sync = api.decode_sync(c.batch, c.n_heads)
+
+    def run_step(self, layer):
+        r = self.lib.pkv_paged_decode_step(
+            self.pool_ref, layer, self.step_ref, self.ptr["q"], self.ptr["k_new"],
+            self.ptr["v_new"], self.case.n_heads, self.scale, self.num_splits, self.ws.data_ptr(),
+            self.ws_bytes, self.sync.data_ptr(), self.sync.numel(), self.out.data_ptr(),
+            self.stream())
+        assert r == 0, r
+
     def layer_of(self, k):
         n = self.case.n_layers
         return (self.case.layer_id - k) % n
@@ -411,11 +434,19 @@ def main():
                              "step_gbps": r.step_bytes() / spp / 1e9,
                              "split_kernel_gbps": r.kernel_bytes() / float(kt_l.mean()) / 1e9,
                              "num_splits": r.num_splits, "graph_ok": ok}
-            log(f"  B=1 L={L}: step {spp * 1e6:.1f} us, split kernel {kt_l.mean() * 1e6:.1f} us")
             if r is not head:
                 del r
                 torch.cuda.empty_cache()
+            rf = FusedDecodeRunner(W.llama_b1_decode(L))
+            spf, okf = timed_graph(rf, 50, 5)
+            sweep[str(L)].update({"fused_step_us": spf * 1e6, "fused_num_splits": rf.num_splits,
+                                  "fused_graph_ok": okf})
+            del rf
+            torch.cuda.empty_cache()
+            log(f"  B=1 L={L}: step {spp * 1e6:.1f} us (fused {spf * 1e6:.1f} us), "
+                f"split kernel {kt_l.mean() * 1e6:.1f} us")
         extra["b1_decode_us"] = {L: v["step_us"] for L, v in sweep.items()}
+        extra["b1_decode_fused_step_us"] = {L: v["fused_step_us"] for L, v in sweep.items()}
         extra["b1_decode_sweep"] = sweep
 
         log("batched prefix-sharing decode")

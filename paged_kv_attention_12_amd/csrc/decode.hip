@@ -262,7 +262,10 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const MergeArgs a) {
   float den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   float M = kNegInf;  // running maximum over the batches seen so far
-  for (int s0 = sg; s0 < S; s0 += SG * KB) {
+  // Every thread runs every batch (the batch holds the workgroup barriers);
+  // split groups past the last split carry weight 0.
+  for (int base = 0; base < S; base += SG * KB) {
+    const int s0 = base + sg;
     float4 ov[KB];
     float mv[KB], lv[KB];
 #pragma unroll
@@ -355,6 +358,9 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, const 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+#ifndef PKV_DEC_P
+#define PKV_DEC_P 2
+#endif
 constexpr int kMfmaD = 128;  // head_dim of the matrix-core path
 constexpr int kKT = 32;      // keys per iteration of a wavefront
 
@@ -368,13 +374,12 @@ constexpr int kKT = 32;      // keys per iteration of a wavefront
 // the same step) instead of the pool.  On return o[e][i] holds the
 // unnormalised O[head c][32g + 8i + e] against the base-2 running max m_run,
 // and l_tot the running sum (both per head, equal in the four lane groups).
-template <int TS, bool NEW>
+template <int TS, bool NEW, int P>
 __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot, int b,
                                             int start, int end, int first, bool active, int hk,
                                             int h0, bool col_ok, const uint16_t *knew,
                                             const uint16_t *vnew, int newpos, f32x4_t (&o)[8],
                                             float &m_run, float &l_tot) {
-  constexpr int P = 2;  // register tile sets (deeper rings measured no faster)
   constexpr int D = kMfmaD;
   constexpr int KT = kKT;
   const int lane = threadIdx.x & 63;
@@ -573,7 +578,7 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs
 
   f32x4_t o[8];
   float m_run, l_tot;
-  attend_mfma<1, false>(a, s_slot, b, start, end, 0, active, hk, h0, col_ok, nullptr, nullptr, -1,
+  attend_mfma<1, false, PKV_DEC_P>(a, s_slot, b, start, end, 0, active, hk, h0, col_ok, nullptr, nullptr, -1,
                         o, m_run, l_tot);
   if (!active || !col_ok) return;
   // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
@@ -661,7 +666,7 @@ __global__ void __launch_bounds__(256, 2) decode_step_kernel(const StepArgs sa) 
 
   f32x4_t o[8];
   float m_run, l_tot;
-  attend_mfma<4, true>(a, s_slot, b, start, end, wave, true, hk, h0, c < ng, knew, vnew, newpos, o,
+  attend_mfma<4, true, PKV_DEC_P>(a, s_slot, b, start, end, wave, true, hk, h0, c < ng, knew, vnew, newpos, o,
                        m_run, l_tot);
 
   // Combine the four waves' states into the split partial.

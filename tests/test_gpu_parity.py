@@ -116,6 +116,29 @@ def test_decode_small_matrix(H, Hk, d, dtype, lens, num_splits):
     assert_close(to_np(out), hv.decode_all(case), dtype, f"{H}/{Hk}/{d}/{dtype}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_with_few_splits_after_lds_heavy_kernel(d):
+    """Regression: with fewer splits than the merge's split groups, every
+    thread must still pass the merge's barriers.  A prefill over huge K/V
+    values runs first, so LDS holds large numbers a skipped write would
+    expose (the merged output then collapsed to 0)."""
+    pf = W.random_case(610 + d, [600, 300], [300, 200], n_heads=32, n_kv_heads=8, head_dim=d,
+                       dtype="bf16")
+    tp = W.make_tensors(pf, device="cuda", poison=False)
+    tp["k_buffer"].fill_(3.0e4)
+    tp["v_buffer"].fill_(-3.0e4)
+    tp["k_new"].fill_(3.0e4)
+    tp["v_new"].fill_(-3.0e4)
+    for s in range(1, 8):
+        gpu_prefill(pf, tp)          # no host sync: the decode follows on the stream
+        case = W.random_case(620 + d + s, [9, 130, 1], n_heads=32, n_kv_heads=8, head_dim=d,
+                             dtype="bf16")
+        t = W.make_tensors(case, device="cuda")
+        hv = HostView(case, t)
+        out = gpu_decode(case, t, num_splits=s)
+        assert_close(to_np(out), hv.decode_all(case), "bf16", f"merge after prefill, splits={s}")
+
+
 def test_decode_single_token_returns_v_exactly():
     case = W.random_case(5, [1, 1, 1], n_heads=8, n_kv_heads=2, head_dim=128, dtype="bf16")
     t = W.make_tensors(case, device="cuda")
