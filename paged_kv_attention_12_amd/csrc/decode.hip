@@ -358,10 +358,8 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, const 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-#ifndef PKV_DEC_P
-#define PKV_DEC_P 2
-#endif
 constexpr int kMfmaD = 128;  // head_dim of the matrix-core path
+constexpr int kRing = 2;     // register tile sets of a wavefront (3 and 4 measured no faster)
 constexpr int kKT = 32;      // keys per iteration of a wavefront
 
 // Online-softmax attention of one wavefront over the keys [start, end) of
@@ -578,7 +576,7 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs
 
   f32x4_t o[8];
   float m_run, l_tot;
-  attend_mfma<1, false, PKV_DEC_P>(a, s_slot, b, start, end, 0, active, hk, h0, col_ok, nullptr, nullptr, -1,
+  attend_mfma<1, false, kRing>(a, s_slot, b, start, end, 0, active, hk, h0, col_ok, nullptr, nullptr, -1,
                         o, m_run, l_tot);
   if (!active || !col_ok) return;
   // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
@@ -666,7 +664,7 @@ __global__ void __launch_bounds__(256, 2) decode_step_kernel(const StepArgs sa) 
 
   f32x4_t o[8];
   float m_run, l_tot;
-  attend_mfma<4, true, PKV_DEC_P>(a, s_slot, b, start, end, wave, true, hk, h0, c < ng, knew, vnew, newpos, o,
+  attend_mfma<4, true, kRing>(a, s_slot, b, start, end, wave, true, hk, h0, c < ng, knew, vnew, newpos, o,
                        m_run, l_tot);
 
   // Combine the four waves' states into the split partial.
