@@ -110,28 +110,6 @@ class DecodeRunner:
         self.merge(st)
 
 
-class FusedDecodeRunner(DecodeRunner):
-    """The same workload stepped through pkv_paged_decode_step: one launch for
-    the K/V write, the split attention and the merge."""
-
-    def __init__(self, case, fill_all_layers=True, num_splits=None):
-        from paged_kv_attention_12_amd import api, binding as B
-        super().__init__(case, fill_all_layers)
-        c = self.case
-        self.num_splits = num_splits or B.pkv_decode_step_pick_splits(
-            c.batch, c.n_kv_heads, c.n_heads, self.step.max_len, self.step.total_len)
-        self.ws = api.decode_workspace(c.batch, c.n_heads, c.head_dim, self.num_splits)
-        self.ws_bytes = self.ws.numel() * 4
-        self.sync = api.decode_sync(c.batch, c.n_heads)
-
-    def run_step(self, layer):
-        r = self.lib.pkv_paged_decode_step(
-            self.pool_ref, layer, self.step_ref, self.ptr["q"], self.ptr["k_new"],
-            self.ptr["v_new"], self.case.n_heads, self.scale, self.num_splits, self.ws.data_ptr(),
-            self.ws_bytes, self.sync.data_ptr(), self.sync.numel(), self.out.data_ptr(),
-            self.stream())
-        assert r == 0, r
-
     def layer_of(self, k):
         n = self.case.n_layers
         return (self.case.layer_id - k) % n
@@ -156,6 +134,29 @@ class FusedDecodeRunner(DecodeRunner):
         c = self.case
         row = c.n_kv_heads * c.head_dim * 2
         return self.kernel_bytes() + 4 * c.batch * row + c.batch * c.n_heads * c.head_dim * 2
+
+
+class FusedDecodeRunner(DecodeRunner):
+    """The same workload stepped through pkv_paged_decode_step: one launch for
+    the K/V write, the split attention and the merge."""
+
+    def __init__(self, case, fill_all_layers=True, num_splits=None):
+        from paged_kv_attention_12_amd import api, binding as B
+        super().__init__(case, fill_all_layers)
+        c = self.case
+        self.num_splits = num_splits or B.pkv_decode_step_pick_splits(
+            c.batch, c.n_kv_heads, c.n_heads, self.step.max_len, self.step.total_len)
+        self.ws = api.decode_workspace(c.batch, c.n_heads, c.head_dim, self.num_splits)
+        self.ws_bytes = self.ws.numel() * 4
+        self.sync = api.decode_sync(c.batch, c.n_heads)
+
+    def run_step(self, layer):
+        r = self.lib.pkv_paged_decode_step(
+            self.pool_ref, layer, self.step_ref, self.ptr["q"], self.ptr["k_new"],
+            self.ptr["v_new"], self.case.n_heads, self.scale, self.num_splits, self.ws.data_ptr(),
+            self.ws_bytes, self.sync.data_ptr(), self.sync.numel(), self.out.data_ptr(),
+            self.stream())
+        assert r == 0, r
 
 
 def graph_steps(runner, n, start=0):
