@@ -73,6 +73,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
   const int b = blockIdx.z;
   const int s = blockIdx.y;
   const int L = a.seq_lens[b];
+  const int pool_row = a.req_pool_indices[b];
   const int start = s * a.chunk;
   const int end = min(L, start + a.chunk);
 
@@ -113,7 +114,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
                      ((int64_t)b * a.n_heads + h0 + g) * D + part * EPL);
   }
 
-  const int32_t *table = a.req_to_token + (int64_t)a.req_pool_indices[b] * a.max_ctx_len;
+  const int32_t *table = a.req_to_token + (int64_t)pool_row * a.max_ctx_len;
   const int64_t row_elems = (int64_t)a.n_kv_heads * D;
   const T *kbase = reinterpret_cast<const T *>(a.k_layer) + (int64_t)hk * D + part * EPL;
   const T *vbase = reinterpret_cast<const T *>(a.v_layer) + (int64_t)hk * D + part * EPL;
@@ -369,11 +370,13 @@ constexpr int kKT = 32;      // keys per iteration of a wavefront
 // within each staged run the wavefront takes the 32-key tiles first,
 // first + TS, first + 2 TS, ...  With NEW the key at position newpos is read
 // from the rows knew / vnew (this kv-head's K and V of the token written in
-// the same step) instead of the pool.  On return o[e][i] holds the
+// the same step) instead of the pool.  pool_row is req_pool_indices[b], read by
+// the caller together with seq_lens[b] so that the two loads share one memory
+// round trip.  On return o[e][i] holds the
 // unnormalised O[head c][32g + 8i + e] against the base-2 running max m_run,
 // and l_tot the running sum (both per head, equal in the four lane groups).
 template <int TS, bool NEW, int P>
-__device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot, int b,
+__device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot, int b, int pool_row,
                                             int start, int end, int first, bool active, int hk,
                                             int h0, bool col_ok, const uint16_t *knew,
                                             const uint16_t *vnew, int newpos, f32x4_t (&o)[8],
@@ -383,6 +386,27 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int g = lane >> 4;
+
+  // Slot ids of a staged run of keys [r0, r0 + run_cap): every thread loads
+  // its SPT entries before any LDS store (one memory round trip per run).
+  // The loads depend on pool_row only, not on seq_lens[b]: entries past the
+  // split's end (clamped to the table row) are staged but never used.
+  const int32_t *table = a.req_to_token + (int64_t)pool_row * a.max_ctx_len;
+  constexpr int SPT = kSlotTile / 256;
+  const int run_cap = min(a.chunk, kSlotTile);
+  int sv[SPT];
+  auto load_run = [&](int r0) {
+#pragma unroll
+    for (int k = 0; k < SPT; ++k)
+      if (256 * k < run_cap)
+        sv[k] = table[min((int64_t)r0 + (int)threadIdx.x + 256 * k, a.max_ctx_len - 1)];
+  };
+  auto store_run = [&]() {
+#pragma unroll
+    for (int k = 0; k < SPT; ++k)
+      if (256 * k < run_cap) s_slot[threadIdx.x + 256 * k] = sv[k];
+  };
+  load_run(start);  // first on the dependent chain to the K/V rows
 
   // Q^T operand: head c, dims 8g + 32k .. +8 for step k.
   uint4 qf[4];
@@ -394,7 +418,6 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
       qf[k] = (active && col_ok) ? load16(qrow + 32 * k) : make_uint4(0u, 0u, 0u, 0u);
   }
 
-  const int32_t *table = a.req_to_token + (int64_t)a.req_pool_indices[b] * a.max_ctx_len;
   const int64_t row_elems = (int64_t)a.n_kv_heads * D;
   const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k_layer) + (int64_t)hk * D + 8 * g;
   const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v_layer) + (int64_t)hk * D + 8 * c;
@@ -498,23 +521,11 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
   uint4 kr[P][2][4], vr[P][8];
   for (int r0 = start; r0 < end; r0 += kSlotTile) {
     const int r1 = min(end, r0 + kSlotTile);
-    if (r0 != start) __syncthreads();
-    {
-      // all of this thread's slot-id loads first, then the LDS stores: one
-      // memory round trip per staged run
-      constexpr int SPT = kSlotTile / 256;
-      int v[SPT];
-#pragma unroll
-      for (int k = 0; k < SPT; ++k) {
-        const int j = r0 + (int)threadIdx.x + 256 * k;
-        v[k] = j < r1 ? table[j] : 0;
-      }
-#pragma unroll
-      for (int k = 0; k < SPT; ++k) {
-        const int j = r0 + (int)threadIdx.x + 256 * k;
-        if (j < r1) s_slot[j - r0] = v[k];
-      }
+    if (r0 != start) {
+      __syncthreads();
+      load_run(r0);
     }
+    store_run();
     __syncthreads();
     if (!active) continue;
     const int round_tiles = (r1 - r0 + KT - 1) / KT;
@@ -545,6 +556,7 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs
   const int b = blockIdx.z;
   const int s = blockIdx.y;
   const int L = a.seq_lens[b];
+  const int pool_row = a.req_pool_indices[b];
   const int start = s * a.chunk;
   const int end = min(L, start + a.chunk);
 
@@ -561,26 +573,16 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs
   const int S = a.num_splits;
   const int64_t pr = ((int64_t)b * a.n_heads + h0 + c) * S + s;  // partial row of head h0 + c
 
-  if (start >= end) {
-    if (active && col_ok) {
-      float4 *o = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) o[x] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (g == 0) {
-        a.ml_part[pr * 2 + 0] = kNegInf;
-        a.ml_part[pr * 2 + 1] = 0.f;
-      }
-    }
-    return;
-  }
-
+  // An empty split (start >= end) runs no tile and writes the empty state
+  // o = 0, m = -inf, l = 0; there is no early exit, so that the loads of
+  // seq_lens[b] and req_pool_indices[b] above issue together.
   f32x4_t o[8];
   float m_run, l_tot;
-  attend_mfma<1, false, kRing>(a, s_slot, b, start, end, 0, active, hk, h0, col_ok, nullptr, nullptr, -1,
-                        o, m_run, l_tot);
+  attend_mfma<1, false, kRing>(a, s_slot, b, pool_row, start, end, 0, active, hk, h0, col_ok, nullptr,
+                               nullptr, -1, o, m_run, l_tot);
   if (!active || !col_ok) return;
   // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
-  const float inv = 1.f / l_tot;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   float4 *op = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -639,6 +641,7 @@ __global__ void __launch_bounds__(256, 2) decode_step_kernel(const StepArgs sa) 
   const int c = lane & 15;
   const int g = lane >> 4;
   const int L = a.seq_lens[b];
+  const int pool_row = a.req_pool_indices[b];
   const int start = s * a.chunk;
   const int end = min(L, start + a.chunk);
   const int hk = task / a.n_chunks;
@@ -664,8 +667,8 @@ __global__ void __launch_bounds__(256, 2) decode_step_kernel(const StepArgs sa) 
 
   f32x4_t o[8];
   float m_run, l_tot;
-  attend_mfma<4, true, kRing>(a, s_slot, b, start, end, wave, true, hk, h0, c < ng, knew, vnew, newpos, o,
-                       m_run, l_tot);
+  attend_mfma<4, true, kRing>(a, s_slot, b, pool_row, start, end, wave, true, hk, h0, c < ng, knew, vnew,
+                              newpos, o, m_run, l_tot);
 
   // Combine the four waves' states into the split partial.
   __syncthreads();  // slot ids are dead
