@@ -159,6 +159,19 @@ class FusedDecodeRunner(DecodeRunner):
         assert r == 0, r
 
 
+class StoredDecodeRunner(DecodeRunner):
+    """The same workload stepped through pkv_paged_decode_store: two launches,
+    the split kernel with the new token's K/V write folded in, then the merge.
+    decode() (used for the split-kernel timing) is the plain split kernel."""
+
+    def run_step(self, layer):
+        r = self.lib.pkv_paged_decode_store(
+            self.pool_ref, layer, self.step_ref, self.ptr["q"], self.ptr["k_new"],
+            self.ptr["v_new"], self.case.n_heads, self.scale, self.num_splits, self.ws.data_ptr(),
+            self.ws_bytes, self.out.data_ptr(), self.stream())
+        assert r == 0, r
+
+
 def graph_steps(runner, n, start=0):
     """Capture n consecutive steps (layer rotation from step `start`) in one graph."""
     torch = runner.torch
@@ -406,7 +419,7 @@ def main():
     # ---- headline: Llama-3-8B-shaped B=1 decode, seq_len 32768 ----
     L_head = W.LLAMA_SWEEP[-1]
     log(f"headline: llama B=1 decode L={L_head}")
-    head = DecodeRunner(W.llama_b1_decode(L_head))
+    head = StoredDecodeRunner(W.llama_b1_decode(L_head))
     sec_per_step, graph_ok = timed_graph(head, args.steps, args.warmup)
     step_bytes = head.step_bytes()
     value = step_bytes / sec_per_step / 1e9
@@ -428,7 +441,7 @@ def main():
     if not args.only_headline:
         sweep = {}
         for L in W.LLAMA_SWEEP:
-            r = head if L == L_head else DecodeRunner(W.llama_b1_decode(L))
+            r = head if L == L_head else StoredDecodeRunner(W.llama_b1_decode(L))
             spp, ok = timed_graph(r, 50, 5)
             kt_l = kernel_event_times(r, 32, reps=2)
             sweep[str(L)] = {"step_us": spp * 1e6, "split_kernel_us": float(kt_l.mean()) * 1e6,
@@ -438,15 +451,22 @@ def main():
             if r is not head:
                 del r
                 torch.cuda.empty_cache()
+            r3 = DecodeRunner(W.llama_b1_decode(L))
+            sp3, ok3 = timed_graph(r3, 50, 5)
+            sweep[str(L)].update({"three_launch_step_us": sp3 * 1e6, "three_launch_graph_ok": ok3})
+            del r3
+            torch.cuda.empty_cache()
             rf = FusedDecodeRunner(W.llama_b1_decode(L))
             spf, okf = timed_graph(rf, 50, 5)
             sweep[str(L)].update({"fused_step_us": spf * 1e6, "fused_num_splits": rf.num_splits,
                                   "fused_graph_ok": okf})
             del rf
             torch.cuda.empty_cache()
-            log(f"  B=1 L={L}: step {spp * 1e6:.1f} us (fused {spf * 1e6:.1f} us), "
-                f"split kernel {kt_l.mean() * 1e6:.1f} us")
+            log(f"  B=1 L={L}: step {spp * 1e6:.1f} us (three launches {sp3 * 1e6:.1f} us, "
+                f"one launch {spf * 1e6:.1f} us), split kernel {kt_l.mean() * 1e6:.1f} us")
         extra["b1_decode_us"] = {L: v["step_us"] for L, v in sweep.items()}
+        extra["b1_decode_three_launch_step_us"] = {L: v["three_launch_step_us"]
+                                                   for L, v in sweep.items()}
         extra["b1_decode_fused_step_us"] = {L: v["fused_step_us"] for L, v in sweep.items()}
         extra["b1_decode_sweep"] = sweep
 
@@ -490,7 +510,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"llama3_8b_shape_b1_decode_L{L_head}", "batch": 1,
                    "n_heads": 32, "n_kv_heads": 8, "head_dim": 128, "seq_len": L_head,
-                   "pool_slots": 65536, "n_layers": 32, "step": "kv_store+paged_decode+merge",
+                   "pool_slots": 65536, "n_layers": 32,
+                   "step": "paged_decode_store (split attention with the new-token K/V write) "
+                           "+ merge",
                    "layer_rotation": "31,30,...,0", "timing": "one HIP graph of K steps",
                    "num_splits": head.num_splits, "bytes_per_step": step_bytes},
         "hbm_frac": value / HBM_PEAK_GBPS,

@@ -246,6 +246,32 @@ pkv_status pkv_paged_decode_step(const pkv_pool *pool, int32_t layer_id, const p
                                  void *workspace, size_t ws_bytes, int32_t *sync,
                                  int64_t sync_len, void *out, void *stream /* hipStream_t */);
 
+/* ----------------------------------------------------------------------
+ * One decode step in two launches (same sources and the same result as
+ * pkv_paged_decode_step): the split attention of pkv_paged_decode with the
+ * new-token K/V write folded in, then pkv_paged_decode_merge into out.
+ *   k_buffer[layer, out_cache_loc[b]] = k_new[b] (same for v), then
+ *   out[b, h] = sum_j softmax_j(q[b,h] . k_j * sm_scale) v_j over the
+ *   seq_lens[b] keys of request b, the new one included.
+ * Decode steps only: step->n_new == batch (one new token per request,
+ * qo_indptr unused).  k_new / v_new: device [batch, n_kv_heads, head_dim],
+ * pool dtype; q, out: device [batch, n_heads, head_dim], pool dtype.
+ * For bf16 pools with head_dim 128 the split kernel attends the new token's
+ * rows straight from k_new / v_new and one wavefront per kv-head writes them
+ * to the pool; this needs out_cache_loc[b] to be the slot of position
+ * seq_lens[b] - 1 of request b with no other position read in this step
+ * mapped to it (fresh slots, as pkv_validate_step checks for duplicates).
+ * Other shapes run pkv_kv_store, pkv_paged_decode and the merge.
+ * workspace / num_splits: as for pkv_paged_decode (pkv_decode_pick_splits,
+ * pkv_decode_workspace_bytes); no counters are needed.
+ * Errors: as pkv_paged_decode, plus PKV_ERR_NULL for missing k_new / v_new /
+ * out / out_cache_loc and PKV_ERR_SHAPE for n_new != batch.
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,
+                                  const void *q, const void *k_new, const void *v_new,
+                                  int32_t n_heads, float sm_scale, int32_t num_splits,
+                                  void *workspace, size_t ws_bytes, void *out, void *stream);
+
 /* Host-only split count for pkv_paged_decode_step: the single-wave choice of
  * pkv_decode_pick_splits divided by four (each split of the fused step is
  * taken by four wavefronts), clamped to [1, max_splits]. */

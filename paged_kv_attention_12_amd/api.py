@@ -97,6 +97,26 @@ def fused_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: Dev
     return out
 
 
+def stored_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q,
+                       k_new, v_new, sm_scale: float, num_splits: Optional[int] = None,
+                       workspace=None, out=None):
+    """The decode step (K/V write, split attention, merge) in two launches: the
+    split kernel also writes the new token's K/V (bf16 pools with head_dim
+    128).  Returns out."""
+    import torch
+    H, d = int(q.shape[1]), int(q.shape[2])
+    if num_splits is None:
+        num_splits = B.pkv_decode_pick_splits(step.batch, int(k_buffer.shape[2]), H,
+                                              step.max_len, step.total_len)
+    if workspace is None:
+        workspace = decode_workspace(step.batch, H, d, num_splits, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    B.pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, k_new, v_new,
+                             sm_scale, num_splits, workspace, out)
+    return out
+
+
 def prefill_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q, k_new,
                  v_new, sm_scale: float, causal: bool = True, out=None, write_kv: bool = True):
     """K/V write of the step's new tokens, then ragged paged prefill."""

@@ -33,7 +33,7 @@ EXPORTED = (
     "pkv_status_string", "pkv_last_hip_error", "pkv_build_step", "pkv_validate_step",
     "pkv_kv_store", "pkv_decode_workspace_bytes", "pkv_decode_pick_splits",
     "pkv_paged_decode", "pkv_paged_decode_merge", "pkv_paged_prefill",
-    "pkv_paged_decode_step", "pkv_decode_step_pick_splits",
+    "pkv_paged_decode_step", "pkv_decode_step_pick_splits", "pkv_paged_decode_store",
 )
 
 
@@ -99,6 +99,8 @@ def load() -> C.CDLL:
         "pkv_paged_decode_step": (C.c_int, [C.POINTER(pkv_pool), i32, C.POINTER(pkv_step), P, P,
                                             P, i32, f32, i32, P, sz, P, i64, P, P]),
         "pkv_decode_step_pick_splits": (i32, [i32, i32, i32, i32, i64, i32]),
+        "pkv_paged_decode_store": (C.c_int, [C.POINTER(pkv_pool), i32, C.POINTER(pkv_step), P, P,
+                                             P, i32, f32, i32, P, sz, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -329,6 +331,25 @@ def pkv_paged_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step:
         _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _dev_ptr(sync, "sync", torch.int32), int(sync.numel()), _dev_ptr(out, "out"), _stream())
     _check(st, "pkv_paged_decode_step")
+
+
+def pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,
+                           k_new, v_new, sm_scale: float, num_splits: int, workspace,
+                           out) -> None:
+    pool = make_pool(k_buffer, v_buffer, req_to_token)
+    if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
+            or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q / out must be [batch, n_heads, head_dim] in the pool dtype")
+    if tuple(k_new.shape) != (step.batch,) + tuple(k_buffer.shape[2:]) \
+            or k_new.shape != v_new.shape or k_new.dtype != k_buffer.dtype \
+            or v_new.dtype != k_buffer.dtype:
+        raise ValueError("k_new / v_new must be [batch, n_kv_heads, head_dim] in the pool dtype")
+    st = load().pkv_paged_decode_store(
+        C.byref(pool), int(layer_id), C.byref(step), _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"),
+        _dev_ptr(v_new, "v_new"), int(q.shape[1]), float(sm_scale), int(num_splits),
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev_ptr(out, "out"), _stream())
+    _check(st, "pkv_paged_decode_store")
 
 
 def pkv_paged_prefill(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,

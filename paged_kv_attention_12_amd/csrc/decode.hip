@@ -549,8 +549,15 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
   l_tot += __shfl_xor(l_tot, 32);
 }
 
-__global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs a) {
+// With NEW the launch also completes the step's K/V write: the new token's
+// rows (position seq_lens[b] - 1) are attended straight from k_new / v_new,
+// and the wavefront of head chunk 0 of each kv-head in the split holding that
+// position writes them to the pool slot out_cache_loc[b] (no wavefront of
+// the launch reads that pool row).
+template <bool NEW>
+__global__ void __launch_bounds__(256) decode_split_mfma_kernel(const StepArgs sa) {
   constexpr int D = kMfmaD;
+  const DecodeArgs &a = sa.d;
   __shared__ int32_t s_slot[kSlotTile];
 
   const int b = blockIdx.z;
@@ -573,13 +580,29 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const DecodeArgs
   const int S = a.num_splits;
   const int64_t pr = ((int64_t)b * a.n_heads + h0 + c) * S + s;  // partial row of head h0 + c
 
+  const int newpos = NEW ? L - 1 : -1;
+  const uint16_t *knew = nullptr, *vnew = nullptr;
+  if constexpr (NEW) {
+    const int64_t new_row = ((int64_t)b * a.n_kv_heads + hk) * D;  // element offset in k_new / v_new
+    knew = reinterpret_cast<const uint16_t *>(sa.k_new) + new_row;
+    vnew = reinterpret_cast<const uint16_t *>(sa.v_new) + new_row;
+    if (active && g0 == 0 && start <= newpos && newpos < end && lane < 2 * D / 8) {
+      const int64_t loc = sa.out_cache_loc[b];
+      const int64_t dst = (loc * a.n_kv_heads + hk) * D + 8 * (lane & 15);
+      if (lane < D / 8)
+        store16(reinterpret_cast<uint16_t *>(sa.k_layer_w) + dst, load16(knew + 8 * (lane & 15)));
+      else
+        store16(reinterpret_cast<uint16_t *>(sa.v_layer_w) + dst, load16(vnew + 8 * (lane & 15)));
+    }
+  }
+
   // An empty split (start >= end) runs no tile and writes the empty state
   // o = 0, m = -inf, l = 0; there is no early exit, so that the loads of
   // seq_lens[b] and req_pool_indices[b] above issue together.
   f32x4_t o[8];
   float m_run, l_tot;
-  attend_mfma<1, false, kRing>(a, s_slot, b, pool_row, start, end, 0, active, hk, h0, col_ok, nullptr,
-                               nullptr, -1, o, m_run, l_tot);
+  attend_mfma<1, NEW, kRing>(a, s_slot, b, pool_row, start, end, 0, active, hk, h0, col_ok, knew, vnew,
+                             newpos, o, m_run, l_tot);
   if (!active || !col_ok) return;
   // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -826,8 +849,10 @@ hipError_t launch_paged_decode(const DecodeArgs &args, int dtype, int head_dim,
   a.n_chunks = (a.group + per_wave - 1) / per_wave;
   a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
   if (mfma) {
+    StepArgs sa{};
+    sa.d = a;
     const dim3 grid((a.n_kv_heads * a.n_chunks + 3) / 4, a.num_splits, a.batch);
-    hipLaunchKernelGGL(decode_split_mfma_kernel, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_split_mfma_kernel<false>, grid, dim3(256), 0, stream, sa);
     return hipGetLastError();
   }
   if (dtype == 1) {
@@ -848,6 +873,16 @@ hipError_t launch_decode_step(const StepArgs &args, hipStream_t stream) {
   sa.tasks = a.n_kv_heads * a.n_chunks;
   const dim3 grid(sa.tasks, a.num_splits, a.batch);
   hipLaunchKernelGGL(decode_step_kernel, grid, dim3(256), 0, stream, sa);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_split_store(const StepArgs &args, hipStream_t stream) {
+  StepArgs sa = args;
+  DecodeArgs &a = sa.d;
+  a.n_chunks = (a.group + 15) / 16;
+  a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
+  const dim3 grid((a.n_kv_heads * a.n_chunks + 3) / 4, a.num_splits, a.batch);
+  hipLaunchKernelGGL(decode_split_mfma_kernel<true>, grid, dim3(256), 0, stream, sa);
   return hipGetLastError();
 }
 

@@ -56,6 +56,10 @@ struct StepArgs {
   int32_t tasks;              // kv-heads x head chunks (set by the launcher)
 };
 hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream);
+// The split attention of one decode step with the new-token K/V write folded
+// in (bf16, head_dim 128); sync, out and tasks are not used.  The merge is a
+// separate launch.
+hipError_t launch_decode_split_store(const StepArgs &a, hipStream_t stream);
 
 struct MergeArgs {
   const float *o_part;

@@ -320,6 +320,62 @@ pkv_status pkv_paged_decode_step(const pkv_pool *pool, int32_t layer_id, const p
   return hip_status(pkv::launch_decode_step(sa, (hipStream_t)stream));
 }
 
+pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,
+                                  const void *q, const void *k_new, const void *v_new,
+                                  int32_t n_heads, float sm_scale, int32_t num_splits,
+                                  void *workspace, size_t ws_bytes, void *out, void *stream) {
+  pkv_status st = check_pool(pool, layer_id);
+  if (st != PKV_OK) return st;
+  if (!step || !q || !workspace || !out) return PKV_ERR_NULL;
+  if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || num_splits <= 0 ||
+      num_splits > 65535 || step->batch > 65535)
+    return PKV_ERR_SHAPE;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(sm_scale)) return PKV_ERR_SHAPE;
+  if (step->batch == 0) return PKV_OK;
+  if (!k_new || !v_new || !step->out_cache_loc || !step->req_pool_indices || !step->seq_lens)
+    return PKV_ERR_NULL;
+  if (step->n_new != step->batch) return PKV_ERR_SHAPE;  // one new token per request
+  if (step->max_len <= 0 || step->max_len > pool->max_ctx_len) return PKV_ERR_SHAPE;
+  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, pool->head_dim, num_splits))
+    return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (pool->dtype != PKV_BF16 || pool->head_dim != 128) {
+    st = pkv_kv_store(pool, layer_id, k_new, v_new, step->out_cache_loc, step->n_new, stream);
+    if (st != PKV_OK) return st;
+    st = pkv_paged_decode(pool, layer_id, step, q, n_heads, sm_scale, num_splits, workspace,
+                          ws_bytes, stream);
+    if (st != PKV_OK) return st;
+  } else {
+    pkv::StepArgs sa{};
+    pkv::DecodeArgs &a = sa.d;
+    a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
+    a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
+    a.req_to_token = pool->req_to_token;
+    a.max_ctx_len = pool->max_ctx_len;
+    a.req_pool_indices = step->req_pool_indices;
+    a.seq_lens = step->seq_lens;
+    a.q = q;
+    a.o_part = reinterpret_cast<float *>(workspace);
+    a.ml_part = a.o_part + (size_t)step->batch * n_heads * num_splits * pool->head_dim;
+    a.batch = step->batch;
+    a.n_heads = n_heads;
+    a.n_kv_heads = pool->n_kv_heads;
+    a.group = n_heads / pool->n_kv_heads;
+    a.num_splits = num_splits;
+    a.chunk = decode_chunk(step->max_len, num_splits);
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    sa.k_new = k_new;
+    sa.v_new = v_new;
+    sa.k_layer_w = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
+    sa.v_layer_w = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
+    sa.out_cache_loc = step->out_cache_loc;
+    st = hip_status(pkv::launch_decode_split_store(sa, (hipStream_t)stream));
+    if (st != PKV_OK) return st;
+  }
+  return pkv_paged_decode_merge(step->batch, n_heads, pool->head_dim, pool->dtype, num_splits,
+                                workspace, ws_bytes, out, stream);
+}
+
 pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_dim,
                                   pkv_dtype out_dtype, int32_t num_splits, const void *workspace,
                                   size_t ws_bytes, void *out, void *stream) {

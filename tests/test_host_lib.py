@@ -243,3 +243,32 @@ def test_fused_step_argument_errors(lib):
     s0.n_new = 2                                          # no out_cache_loc
     assert call(step=s0) == B.PKV_ERR_NULL
     assert call(pool=_fake_pool(head_dim=96)) == B.PKV_ERR_UNSUPPORTED
+
+
+def test_stored_step_argument_errors(lib):
+    """Host checks of pkv_paged_decode_store; nothing reaches the device."""
+    p = _fake_pool()
+    s = B.pkv_step()
+    s.batch, s.req_pool_indices, s.seq_lens, s.max_len = 2, 0x10, 0x20, 8
+    s.out_cache_loc, s.n_new = 0x30, 2
+    fake = C.c_void_p(0x4000)
+    need = lib.pkv_decode_workspace_bytes(2, 4, 128, 4)
+    call = lambda step=s, pool=p, ws=need, ns=4, out=fake, knew=fake: \
+        lib.pkv_paged_decode_store(C.byref(pool), 0, C.byref(step), fake, knew, fake, 4, 0.1, ns,
+                                   fake, ws, out, None)
+    assert call(out=None) == B.PKV_ERR_NULL
+    assert call(knew=None) == B.PKV_ERR_NULL
+    assert call(ws=need - 1) == B.PKV_ERR_WORKSPACE_TOO_SMALL
+    assert call(ns=0) == B.PKV_ERR_SHAPE
+    s3 = B.pkv_step()
+    s3.batch, s3.req_pool_indices, s3.seq_lens, s3.max_len = 2, 0x10, 0x20, 8
+    s3.out_cache_loc, s3.n_new = 0x30, 3                  # not one new token per request
+    assert call(step=s3) == B.PKV_ERR_SHAPE
+    s0 = B.pkv_step()
+    s0.batch, s0.req_pool_indices, s0.seq_lens, s0.max_len = 2, 0x10, 0x20, 8
+    s0.n_new = 2                                          # no out_cache_loc
+    assert call(step=s0) == B.PKV_ERR_NULL
+    assert call(pool=_fake_pool(head_dim=96)) == B.PKV_ERR_UNSUPPORTED
+    sb = B.pkv_step()
+    sb.batch = 0                                          # empty step: nothing to do
+    assert call(step=sb) == B.PKV_OK
