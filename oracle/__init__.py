@@ -24,3 +24,4 @@ from .attention import (  # noqa: F401
     split_partial,
     validate_step,
 )
+from .rope import round_to_bf16, rope_kv_store, rope_rotate, to_dtype  # noqa: F401

@@ -61,7 +61,10 @@ def build_step(req_pool_indices: Sequence[int], seq_lens: Sequence[int],
     request b's new tokens sit at the last q_len_b logical positions of its
     context, so token t maps to req_to_token[r_b, seq_len_b - q_len_b + t].
     prefill_order lists the requests longest context first (ties in batch
-    order); it only schedules work.  Returns a dict of int32 arrays and ints.
+    order); it only schedules work.  position_ids lists, in qo order, the
+    logical position seq_len_b - q_len_b + t of every new token: the row of
+    the rotary table its query and key use ("Inference" guide, section
+    "Rotary Embedding Backend").  Returns a dict of int32 arrays and ints.
     """
     B = len(seq_lens)
     if q_lens is None:
@@ -69,6 +72,7 @@ def build_step(req_pool_indices: Sequence[int], seq_lens: Sequence[int],
     kv_indptr = [0]
     qo_indptr = [0]
     locs: List[int] = []
+    poss: List[int] = []
     for b in range(B):
         r = int(req_pool_indices[b])
         L = int(seq_lens[b])
@@ -77,12 +81,14 @@ def build_step(req_pool_indices: Sequence[int], seq_lens: Sequence[int],
         qo_indptr.append(qo_indptr[-1] + ql)
         for t in range(ql):
             locs.append(int(req_to_token[r, L - ql + t]))
+            poss.append(L - ql + t)
     # processing order for prefill: longest context first, ties in batch order
     order = sorted(range(B), key=lambda b: (-int(seq_lens[b]), b))
     return {
         "kv_indptr": np.array(kv_indptr, dtype=np.int32),
         "qo_indptr": np.array(qo_indptr, dtype=np.int32),
         "out_cache_loc": np.array(locs, dtype=np.int32),
+        "position_ids": np.array(poss, dtype=np.int32),
         "prefill_order": np.array(order, dtype=np.int32),
         "max_len": max([int(x) for x in seq_lens], default=0),
         "max_q_len": max([int(x) for x in q_lens], default=0),
