@@ -119,6 +119,18 @@ pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices,
                           int64_t out_cache_loc_cap, int64_t *n_new,
                           int32_t *max_len, int32_t *max_q_len, int32_t *prefill_order);
 
+/* Host: the logical position of every new token of a step, in qo order
+ * (the rows of the rotary table its query and key use; "Inference" guide,
+ * section "Rotary Embedding Backend": the table is indexed by
+ * position_ids).  Request b's new tokens are its last q_len_b positions:
+ * token t sits at seq_len_b - q_len_b + t.  All pointers are HOST memory;
+ * q_lens NULL means one new token per request (decode).  Writes *n_new
+ * entries of position_ids (capacity `capacity`).  PKV_ERR_BAD_METADATA when
+ * a q_len is negative or above its seq_len, PKV_ERR_SHAPE when capacity is
+ * too small. */
+pkv_status pkv_build_positions(int32_t batch, const int32_t *seq_lens, const int32_t *q_lens,
+                               int32_t *position_ids, int64_t capacity, int64_t *n_new);
+
 /* Checked mode: validates HOST copies of one step's metadata against a pool
  * of `size` slots.  Accepts (PKV_OK) iff every request row is in
  * [0, num_reqs), every seq_len in [1, max_ctx_len], every q_len in
@@ -208,6 +220,37 @@ pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_d
                                   pkv_dtype out_dtype, int32_t num_splits,
                                   const void *workspace, size_t ws_bytes, void *out,
                                   void *stream /* hipStream_t */);
+
+/* ------------------------------------------------------------------------
+ * Rotary embedding of one forward's new tokens fused with their K/V write
+ * ("Inference" guide, section "Rotary Embedding Backend": freqs_cis
+ * [max_len, dim/2, 2] f32 holds [cos, sin] pairs, the rows used are those of
+ * position_ids, and adjacent elements (2j, 2j+1) form one complex number
+ * multiplied by cos + i sin; section "KV Cache": keys are rotated before the
+ * cache write, values are not rotated).  For every new token i at position
+ * p = position_ids[i] and every pair j of every head row:
+ *   (x[2j], x[2j+1]) -> (x[2j] c - x[2j+1] s, x[2j] s + x[2j+1] c),
+ *   (c, s) = freqs_cis[p, j],
+ * computed in fp32 and rounded once to the pool dtype (bf16: to nearest,
+ * ties to even).  Queries: q -> q_out (q_out may equal q).  Keys: the rotated
+ * row i goes to slot out_cache_loc[i] of layer layer_id; values: v_new row i
+ * is copied there bit for bit.  No other byte of the pool changes.
+ * q, q_out: device [n_new, n_heads, head_dim]; k_new, v_new: device
+ * [n_new, n_kv_heads, head_dim]; all in the pool dtype, 16-byte aligned.
+ * position_ids, out_cache_loc: device int32 [n_new] (pkv_build_positions and
+ * pkv_build_step give them in the same qo order).  freqs_cis: device f32
+ * [max_pos, head_dim/2, 2], 16-byte aligned.  The caller guarantees positions
+ * in [0, max_pos) (others read the nearest row) and distinct slots in
+ * [0, size).  n_new == 0 is a no-op.
+ * Errors: PKV_ERR_NULL (missing pointer), PKV_ERR_SHAPE (n_heads not a
+ * positive multiple of n_kv_heads, max_pos <= 0, n_new < 0, misaligned
+ * pointer), PKV_ERR_UNSUPPORTED (head_dim other than 64 / 128).
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_rope_kv_store(const pkv_pool *pool, int32_t layer_id, const void *q, void *q_out,
+                             int32_t n_heads, const void *k_new, const void *v_new,
+                             const int32_t *position_ids, const float *freqs_cis,
+                             int64_t max_pos, const int32_t *out_cache_loc, int64_t n_new,
+                             void *stream);
 
 /* ------------------------------------------------------------------------
  * One decode step in one launch ("Inference" guide, section "KVCache System":

@@ -35,6 +35,9 @@ class DeviceStep:
         self.out_cache_loc = to(md["out_cache_loc"]) if self.n_new else \
             torch.zeros(0, dtype=torch.int32, device=device)
         self.prefill_order = to(md["prefill_order"]) if self.batch else None
+        # logical positions of the new tokens (rows of the rotary table)
+        self.position_ids = to(B.pkv_build_positions(seq_lens, q_lens)) if self.n_new else \
+            torch.zeros(0, dtype=torch.int32, device=device)
         self.c = B.make_step(self.batch, self.req_pool_indices, self.seq_lens, self.kv_indptr,
                              None if self.decode else self.qo_indptr,
                              self.out_cache_loc if self.n_new else None, self.n_new,
@@ -115,6 +118,20 @@ def stored_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: De
     B.pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, k_new, v_new,
                              sm_scale, num_splits, workspace, out)
     return out
+
+
+def rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q, k_new,
+                  v_new, freqs_cis, q_out=None):
+    """Rotate the step's new queries and keys by their positions' rows of the
+    rotary table freqs_cis [max_pos, head_dim / 2, 2] (f32 [cos, sin]) and
+    write the rotated keys and the values to the pool, in one launch.
+    Returns the rotated queries (q_out; pass q_out=q to rotate in place)."""
+    import torch
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    B.pkv_rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id, q, q_out, k_new, v_new,
+                        step.position_ids, freqs_cis, step.out_cache_loc)
+    return q_out
 
 
 def prefill_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q, k_new,

@@ -34,6 +34,7 @@ EXPORTED = (
     "pkv_kv_store", "pkv_decode_workspace_bytes", "pkv_decode_pick_splits",
     "pkv_paged_decode", "pkv_paged_decode_merge", "pkv_paged_prefill",
     "pkv_paged_decode_step", "pkv_decode_step_pick_splits", "pkv_paged_decode_store",
+    "pkv_build_positions", "pkv_rope_kv_store",
 )
 
 
@@ -101,6 +102,9 @@ def load() -> C.CDLL:
         "pkv_decode_step_pick_splits": (i32, [i32, i32, i32, i32, i64, i32]),
         "pkv_paged_decode_store": (C.c_int, [C.POINTER(pkv_pool), i32, C.POINTER(pkv_step), P, P,
                                              P, i32, f32, i32, P, sz, P, P]),
+        "pkv_build_positions": (C.c_int, [i32, P, P, P, i64, C.POINTER(C.c_int64)]),
+        "pkv_rope_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, i32, P, P, P, P, i64, P,
+                                        i64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -234,6 +238,21 @@ def pkv_build_step(req_pool_indices, seq_lens, req_to_token, q_lens=None) -> dic
             "prefill_order": order[:B].copy()}
 
 
+def pkv_build_positions(seq_lens, q_lens=None) -> np.ndarray:
+    """Host: logical position of every new token, in qo order (int32)."""
+    sl = _host_i32(seq_lens, "seq_lens")
+    ql = _host_i32(q_lens, "q_lens")
+    B = len(sl)
+    if ql is not None and len(ql) != B:
+        raise ValueError("batch arrays differ in length")
+    cap = int(ql.sum()) if ql is not None else B
+    pos = np.zeros(max(cap, 1), dtype=np.int32)
+    n_new = C.c_int64(0)
+    st = load().pkv_build_positions(B, _hp(sl), _hp(ql), _hp(pos), cap, C.byref(n_new))
+    _check(st, "pkv_build_positions")
+    return pos[:n_new.value].copy()
+
+
 def pkv_validate_step(size: int, req_to_token, req_pool_indices, seq_lens, kv_indptr,
                       qo_indptr, out_cache_loc, prefill_order=None) -> int:
     """Checked mode on host copies; returns the status (0 = well formed)."""
@@ -350,6 +369,31 @@ def pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id: int, step
         _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _dev_ptr(out, "out"), _stream())
     _check(st, "pkv_paged_decode_store")
+
+
+def pkv_rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, q, q_out, k_new, v_new,
+                      position_ids, freqs_cis, out_cache_loc) -> None:
+    import torch
+    pool = make_pool(k_buffer, v_buffer, req_to_token)
+    n_new = int(k_new.shape[0])
+    if q.dim() != 3 or q.shape[0] != n_new or q.shape[2] != k_buffer.shape[3] \
+            or q.dtype != k_buffer.dtype or q_out.shape != q.shape or q_out.dtype != q.dtype:
+        raise ValueError("q / q_out must be [n_new, n_heads, head_dim] in the pool dtype")
+    if tuple(k_new.shape[1:]) != tuple(k_buffer.shape[2:]) or k_new.shape != v_new.shape \
+            or k_new.dtype != k_buffer.dtype or v_new.dtype != k_buffer.dtype:
+        raise ValueError("k_new / v_new must be [n_new, n_kv_heads, head_dim] in the pool dtype")
+    if freqs_cis.dim() != 3 or freqs_cis.shape[1:] != (k_buffer.shape[3] // 2, 2) \
+            or freqs_cis.dtype != torch.float32:
+        raise ValueError("freqs_cis must be float32 [max_pos, head_dim / 2, 2]")
+    if position_ids.numel() != n_new or out_cache_loc.numel() != n_new:
+        raise ValueError("position_ids / out_cache_loc must hold n_new entries")
+    st = load().pkv_rope_kv_store(
+        C.byref(pool), int(layer_id), _dev_ptr(q, "q"), _dev_ptr(q_out, "q_out"), int(q.shape[1]),
+        _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
+        _dev_ptr(position_ids, "position_ids", torch.int32),
+        _dev_ptr(freqs_cis, "freqs_cis", torch.float32), int(freqs_cis.shape[0]),
+        _dev_ptr(out_cache_loc, "out_cache_loc", torch.int32), n_new, _stream())
+    _check(st, "pkv_rope_kv_store")
 
 
 def pkv_paged_prefill(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,

@@ -61,6 +61,26 @@ hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream);
 // separate launch.
 hipError_t launch_decode_split_store(const StepArgs &a, hipStream_t stream);
 
+// Rotary embedding of the new tokens fused with their K/V write.
+struct RopeArgs {
+  const void *q;              // [n_new, n_heads, head_dim], pool dtype
+  void *q_out;                // same shape; may equal q
+  const void *k_new;          // [n_new, n_kv_heads, head_dim]
+  const void *v_new;
+  void *k_layer;              // layer layer_id of the pool (writable)
+  void *v_layer;
+  const int32_t *position_ids;  // [n_new]
+  const float *freqs;         // [max_pos, head_dim / 2, 2]: [cos, sin]
+  int64_t max_pos;
+  const int32_t *out_cache_loc;  // [n_new]
+  int64_t n_new;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+};
+// dtype: 0 = f32, 1 = bf16
+hipError_t launch_rope_kv_store(const RopeArgs &a, int dtype, hipStream_t stream);
+
 struct MergeArgs {
   const float *o_part;
   const float *ml_part;

@@ -112,6 +112,25 @@ pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices, const 
   return PKV_OK;
 }
 
+pkv_status pkv_build_positions(int32_t batch, const int32_t *seq_lens, const int32_t *q_lens,
+                               int32_t *position_ids, int64_t capacity, int64_t *n_new) {
+  if (batch < 0) return PKV_ERR_SHAPE;
+  if (!n_new) return PKV_ERR_NULL;
+  if (batch > 0 && !seq_lens) return PKV_ERR_NULL;
+  int64_t qo = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t L = seq_lens[b];
+    const int32_t ql = q_lens ? q_lens[b] : 1;
+    if (ql < 0 || ql > L) return PKV_ERR_BAD_METADATA;
+    if (qo + ql > capacity) return PKV_ERR_SHAPE;
+    if (ql > 0 && !position_ids) return PKV_ERR_NULL;
+    for (int32_t t = 0; t < ql; ++t) position_ids[qo + t] = L - ql + t;
+    qo += ql;
+  }
+  *n_new = qo;
+  return PKV_OK;
+}
+
 pkv_status pkv_validate_step(int64_t size, int64_t num_reqs, int64_t max_ctx_len,
                              const int32_t *req_to_token, int32_t batch,
                              const int32_t *req_pool_indices, const int32_t *seq_lens,
@@ -374,6 +393,42 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
   }
   return pkv_paged_decode_merge(step->batch, n_heads, pool->head_dim, pool->dtype, num_splits,
                                 workspace, ws_bytes, out, stream);
+}
+
+pkv_status pkv_rope_kv_store(const pkv_pool *pool, int32_t layer_id, const void *q, void *q_out,
+                             int32_t n_heads, const void *k_new, const void *v_new,
+                             const int32_t *position_ids, const float *freqs_cis,
+                             int64_t max_pos, const int32_t *out_cache_loc, int64_t n_new,
+                             void *stream) {
+  pkv_status st = check_pool(pool, layer_id);
+  if (st != PKV_OK) return st;
+  if (n_new < 0 || max_pos <= 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0)
+    return PKV_ERR_SHAPE;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (n_new == 0) return PKV_OK;
+  if (!q || !q_out || !k_new || !v_new || !position_ids || !freqs_cis || !out_cache_loc)
+    return PKV_ERR_NULL;
+  auto aligned = [](const void *p) { return ((uintptr_t)p & 15u) == 0; };
+  if (!aligned(q) || !aligned(q_out) || !aligned(k_new) || !aligned(v_new) || !aligned(freqs_cis))
+    return PKV_ERR_SHAPE;
+  if (n_new > INT32_MAX) return PKV_ERR_SHAPE;
+  pkv::RopeArgs a;
+  a.q = q;
+  a.q_out = q_out;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_layer = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
+  a.v_layer = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
+  a.position_ids = position_ids;
+  a.freqs = freqs_cis;
+  a.max_pos = max_pos;
+  a.out_cache_loc = out_cache_loc;
+  a.n_new = n_new;
+  a.n_heads = n_heads;
+  a.n_kv_heads = pool->n_kv_heads;
+  a.head_dim = pool->head_dim;
+  return hip_status(pkv::launch_rope_kv_store(a, pool->dtype == PKV_BF16 ? 1 : 0,
+                                              (hipStream_t)stream));
 }
 
 pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_dim,

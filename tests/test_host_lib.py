@@ -272,3 +272,47 @@ def test_stored_step_argument_errors(lib):
     sb = B.pkv_step()
     sb.batch = 0                                          # empty step: nothing to do
     assert call(step=sb) == B.PKV_OK
+
+
+def test_build_positions_matches_oracle():
+    import oracle
+    import workloads as W
+    for seed, lens, qls in [(1, [5, 1, 9], [2, 1, 9]), (2, [7, 300, 64], None), (3, [4, 4], [0, 4])]:
+        case = W.random_case(seed, lens, qls, n_heads=2, n_kv_heads=1, head_dim=4)
+        md = oracle.build_step(case.req_pool_indices, case.seq_lens, case.req_to_token,
+                               None if qls is None else case.q_lens)
+        got = B.pkv_build_positions(case.seq_lens, None if qls is None else case.q_lens)
+        assert np.array_equal(got, md["position_ids"])
+
+
+def test_build_positions_errors(lib):
+    sl = np.array([3, 2], dtype=np.int32)
+    bad = np.array([1, 3], dtype=np.int32)        # q_len above seq_len
+    out = np.zeros(8, dtype=np.int32)
+    n = C.c_int64(0)
+    p = lambda a: a.ctypes.data_as(C.c_void_p)
+    assert lib.pkv_build_positions(2, p(sl), p(bad), p(out), 8, C.byref(n)) == B.PKV_ERR_BAD_METADATA
+    assert lib.pkv_build_positions(2, p(sl), None, p(out), 1, C.byref(n)) == B.PKV_ERR_SHAPE
+    assert lib.pkv_build_positions(2, None, None, p(out), 8, C.byref(n)) == B.PKV_ERR_NULL
+    assert lib.pkv_build_positions(-1, p(sl), None, p(out), 8, C.byref(n)) == B.PKV_ERR_SHAPE
+    assert lib.pkv_build_positions(2, p(sl), None, p(out), 8, C.byref(n)) == B.PKV_OK
+    assert n.value == 2 and out[:2].tolist() == [2, 1]
+
+
+def test_rope_kv_store_argument_errors(lib):
+    """Host checks of pkv_rope_kv_store; nothing reaches the device."""
+    p = _fake_pool()
+    fake = C.c_void_p(0x4000)
+    mis = C.c_void_p(0x4008)                       # 8-byte, not 16-byte, aligned
+    call = lambda pool=p, q=fake, qo=fake, H=4, kn=fake, pos=fake, fr=fake, mp=16, n=3: \
+        lib.pkv_rope_kv_store(C.byref(pool), 0, q, qo, H, kn, fake, pos, fr, mp, fake, n, None)
+    assert call(q=None) == B.PKV_ERR_NULL
+    assert call(pos=None) == B.PKV_ERR_NULL
+    assert call(fr=None) == B.PKV_ERR_NULL
+    assert call(q=mis) == B.PKV_ERR_SHAPE
+    assert call(fr=mis) == B.PKV_ERR_SHAPE
+    assert call(mp=0) == B.PKV_ERR_SHAPE
+    assert call(H=3) == B.PKV_ERR_SHAPE               # not a multiple of n_kv_heads
+    assert call(n=-1) == B.PKV_ERR_SHAPE
+    assert call(pool=_fake_pool(head_dim=96)) == B.PKV_ERR_UNSUPPORTED
+    assert call(n=0) == B.PKV_OK                      # empty step: nothing to do

@@ -307,6 +307,18 @@ def make_tensors(case: Case, device="cpu", poison: bool = True) -> Dict[str, obj
     }
 
 
+def rope_table(max_pos: int, head_dim: int, base: float = 10000.0, device="cpu"):
+    """A rotary table input, float32 [max_pos, head_dim / 2, 2] of [cos, sin]
+    for the angles p * base^(-2j / head_dim) (how a model fills its table is
+    outside the rotary step; this is the usual construction)."""
+    import torch
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    inv = base ** (-2.0 * j / head_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    t = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    return torch.from_numpy(t).to(device)
+
+
 def named_cases() -> List[str]:
     return ["tiny_decode_f32", "llama_b1_decode", "batched_prefix_decode",
             "ragged_prefill", "long_context_decode"]
