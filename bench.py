@@ -276,6 +276,16 @@ def bench_prefill(reps=20):
         assert lib.pkv_paged_prefill(C.byref(pool), 0, C.byref(step.c), t["q"].data_ptr(),
                                      case.n_heads, case.sm_scale, 1, out.data_ptr(), st) == 0
 
+    freqs = W.rope_table(case.max_ctx_len, case.head_dim, device="cuda")
+    q_rot = torch.empty_like(t["q"])
+
+    def rope():
+        assert lib.pkv_rope_kv_store(C.byref(pool), 0, t["q"].data_ptr(), q_rot.data_ptr(),
+                                     case.n_heads, t["k_new"].data_ptr(), t["v_new"].data_ptr(),
+                                     step.position_ids.data_ptr(), freqs.data_ptr(),
+                                     freqs.shape[0], step.out_cache_loc.data_ptr(), step.n_new,
+                                     st) == 0
+
     for _ in range(3):
         store()
         attend()
@@ -291,6 +301,22 @@ def bench_prefill(reps=20):
     torch.cuda.synchronize()
     t_store = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e-3
     t_pre = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e-3
+    for _ in range(3):
+        rope()
+    torch.cuda.synchronize()
+    evr = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evr:
+        a.record(cur)
+        rope()
+        b.record(cur)
+    torch.cuda.synchronize()
+    t_rope = float(np.median([a.elapsed_time(b) for a, b in evr])) * 1e-3
+    n = step.n_new
+    # q, k, v rows read and written once, positions and slots read, one
+    # table row (head_dim / 2 [cos, sin] f32 pairs) per token
+    rope_bytes = (2 * n * (case.n_heads + 2 * case.n_kv_heads) * case.head_dim * 2 + 8 * n
+                  + n * case.head_dim * 4)
     flops = prefill_flops(case)
     med = float(np.median(t_pre))
     row = case.n_kv_heads * case.head_dim * 2
@@ -302,6 +328,9 @@ def bench_prefill(reps=20):
         "tflops": flops / med / 1e12, "frac_of_bf16_peak": flops / med / 1e12 / BF16_PEAK_TFLOPS,
         "kv_store_ms": float(np.median(t_store)) * 1e3,
         "kv_store_gbps": 4 * step.n_new * row / float(np.median(t_store)) / 1e9,
+        "rope_kv_store_ms": t_rope * 1e3, "rope_kv_store_bytes": rope_bytes,
+        "rope_kv_store_gbps": rope_bytes / t_rope / 1e9,
+        "rope_kv_store_frac_of_hbm_peak": rope_bytes / t_rope / 1e9 / HBM_PEAK_GBPS,
     }
 
 
