@@ -68,7 +68,11 @@ typedef struct {
 
 /* One step's KVCache metadata (same section).  Arrays are device pointers;
  * n_new, max_len and max_q_len are host values (max_len exists so that no
- * device->host read is needed to size the decode launch). */
+ * device->host read is needed to size the decode launch).  For decode,
+ * max_len may be any bound of seq_lens up to max_ctx_len, not only their
+ * maximum: the kernels read seq_lens from device memory, so a captured graph
+ * can replay steps whose lengths (and out_cache_loc, position_ids) the
+ * caller advances in place between replays. */
 typedef struct {
   int32_t batch;
   const int32_t *req_pool_indices;  /* [batch] row of req_to_token per request        */
@@ -77,7 +81,7 @@ typedef struct {
   const int32_t *qo_indptr;         /* [batch+1] exclusive prefix sum of q_lens; decode may pass NULL */
   const int32_t *out_cache_loc;     /* [n_new] write slots in qo order                 */
   int64_t n_new;                    /* total new tokens (decode: batch)                */
-  int32_t max_len;                  /* max(seq_lens)                                   */
+  int32_t max_len;                  /* max(seq_lens), or for decode any bound of them  */
   int32_t max_q_len;                /* max(q_lens) (decode: 1)                         */
   const int32_t *prefill_order;     /* [batch] or NULL: order in which prefill takes the
                                        requests (a permutation of 0..batch-1, e.g. the

@@ -17,13 +17,14 @@ class DeviceStep:
     request rows and lengths), with the host scalars kept alongside."""
 
     def __init__(self, req_pool_indices, seq_lens, req_to_token_host, q_lens=None,
-                 device="cuda"):
+                 device="cuda", max_len: Optional[int] = None):
         import torch
         md = B.pkv_build_step(req_pool_indices, seq_lens, req_to_token_host, q_lens)
         self.host = md
         self.batch = len(md["kv_indptr"]) - 1
         self.n_new = md["n_new"]
-        self.max_len = md["max_len"]
+        # decode: a larger bound lets graph replays grow seq_lens in place
+        self.max_len = md["max_len"] if max_len is None else max(int(max_len), md["max_len"])
         self.max_q_len = md["max_q_len"]
         self.total_len = int(md["kv_indptr"][-1])
         self.decode = q_lens is None
