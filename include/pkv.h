@@ -226,6 +226,25 @@ pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_d
                                   void *stream /* hipStream_t */);
 
 /* ------------------------------------------------------------------------
+ * In-place advance of a decode step's device metadata to the next token
+ * (commit history of the pages: decode metadata such as position_ids,
+ * seq_lens and kv_indptr is updated in place from step to step instead of
+ * being rebuilt, so that a captured graph can be replayed).  One launch:
+ *   seq_lens[b] += 1; position_ids[b] = seq_lens[b] - 1 (if not NULL);
+ *   out_cache_loc[b] = req_to_token[req_pool_indices[b], seq_lens[b] - 1];
+ *   kv_indptr[b] += b for b in [0, batch] (if not NULL).
+ * All arrays are device int32 owned by the caller; the caller keeps every
+ * length within max_ctx_len (a position past the row reads the row's last
+ * entry instead).  The host max_len of the step must already bound the
+ * lengths the next steps reach.  batch == 0 is a no-op.
+ * Errors: PKV_ERR_NULL (missing seq_lens / req_pool_indices / out_cache_loc),
+ * PKV_ERR_SHAPE (batch < 0).
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_decode_advance(const pkv_pool *pool, int32_t batch, const int32_t *req_pool_indices,
+                              int32_t *seq_lens, int32_t *kv_indptr, int32_t *out_cache_loc,
+                              int32_t *position_ids, void *stream);
+
+/* ------------------------------------------------------------------------
  * Rotary embedding of one forward's new tokens fused with their K/V write
  * ("Inference" guide, section "Rotary Embedding Backend": freqs_cis
  * [max_len, dim/2, 2] f32 holds [cos, sin] pairs, the rows used are those of

@@ -121,6 +121,14 @@ def stored_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: De
     return out
 
 
+def advance_decode(k_buffer, v_buffer, req_to_token, step: DeviceStep) -> None:
+    """Move a decode step's device metadata to the next token in place (one
+    launch; graph-capturable).  step.max_len must already bound the lengths
+    the coming steps reach (DeviceStep(..., max_len=...))."""
+    B.pkv_decode_advance(k_buffer, v_buffer, req_to_token, step.req_pool_indices, step.seq_lens,
+                         step.kv_indptr, step.out_cache_loc, step.position_ids)
+
+
 def rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q, k_new,
                   v_new, freqs_cis, q_out=None):
     """Rotate the step's new queries and keys by their positions' rows of the

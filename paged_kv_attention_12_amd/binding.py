@@ -34,7 +34,7 @@ EXPORTED = (
     "pkv_kv_store", "pkv_decode_workspace_bytes", "pkv_decode_pick_splits",
     "pkv_paged_decode", "pkv_paged_decode_merge", "pkv_paged_prefill",
     "pkv_paged_decode_step", "pkv_decode_step_pick_splits", "pkv_paged_decode_store",
-    "pkv_build_positions", "pkv_rope_kv_store",
+    "pkv_build_positions", "pkv_rope_kv_store", "pkv_decode_advance",
 )
 
 
@@ -105,6 +105,7 @@ def load() -> C.CDLL:
         "pkv_build_positions": (C.c_int, [i32, P, P, P, i64, C.POINTER(C.c_int64)]),
         "pkv_rope_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, i32, P, P, P, P, i64, P,
                                         i64, P]),
+        "pkv_decode_advance": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -394,6 +395,23 @@ def pkv_rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, q, q_out,
         _dev_ptr(freqs_cis, "freqs_cis", torch.float32), int(freqs_cis.shape[0]),
         _dev_ptr(out_cache_loc, "out_cache_loc", torch.int32), n_new, _stream())
     _check(st, "pkv_rope_kv_store")
+
+
+def pkv_decode_advance(k_buffer, v_buffer, req_to_token, req_pool_indices, seq_lens, kv_indptr,
+                       out_cache_loc, position_ids) -> None:
+    import torch
+    pool = make_pool(k_buffer, v_buffer, req_to_token)
+    n = int(seq_lens.numel())
+    if req_pool_indices.numel() != n or out_cache_loc.numel() != n or \
+            (position_ids is not None and position_ids.numel() != n) or \
+            (kv_indptr is not None and kv_indptr.numel() != n + 1):
+        raise ValueError("decode metadata arrays disagree in length")
+    st = load().pkv_decode_advance(
+        C.byref(pool), n, _dev_ptr(req_pool_indices, "req_pool_indices", torch.int32),
+        _dev_ptr(seq_lens, "seq_lens", torch.int32), _dev_ptr(kv_indptr, "kv_indptr", torch.int32),
+        _dev_ptr(out_cache_loc, "out_cache_loc", torch.int32),
+        _dev_ptr(position_ids, "position_ids", torch.int32), _stream())
+    _check(st, "pkv_decode_advance")
 
 
 def pkv_paged_prefill(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,

@@ -45,4 +45,29 @@ hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t stream) {
   return go(uint16_t{}, 2);
 }
 
+// Advance of a decode step's metadata to the next token, in place: every
+// request grows by one token, its new token sits at position seq_len - 1 and
+// is written to that position's slot; kv_indptr (the prefix sums of seq_lens)
+// moves by b at entry b.  Positions past the table row are clamped (the
+// caller keeps lengths within max_ctx_len; the clamp keeps reads in bounds).
+__global__ void __launch_bounds__(256) decode_advance_kernel(const AdvanceArgs a) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b > a.batch) return;
+  if (b < a.batch) {
+    const int32_t L = a.seq_lens[b] + 1;
+    a.seq_lens[b] = L;
+    if (a.position_ids) a.position_ids[b] = L - 1;
+    const int64_t col = min((int64_t)L - 1, a.max_ctx_len - 1);
+    a.out_cache_loc[b] = a.req_to_token[(int64_t)a.req_pool_indices[b] * a.max_ctx_len + col];
+  }
+  if (a.kv_indptr) a.kv_indptr[b] += b;
+}
+
+hipError_t launch_decode_advance(const AdvanceArgs &a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  const int blocks = (a.batch + 1 + 255) / 256;
+  hipLaunchKernelGGL(decode_advance_kernel, dim3(blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

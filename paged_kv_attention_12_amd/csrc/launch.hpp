@@ -19,6 +19,19 @@ struct KvStoreArgs {
 };
 hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t stream);
 
+// In-place advance of a decode step's metadata to the next token.
+struct AdvanceArgs {
+  const int32_t *req_to_token;
+  int64_t max_ctx_len;
+  const int32_t *req_pool_indices;  // [batch]
+  int32_t *seq_lens;                // [batch]
+  int32_t *kv_indptr;               // [batch + 1] or null
+  int32_t *out_cache_loc;           // [batch]
+  int32_t *position_ids;            // [batch] or null
+  int32_t batch;
+};
+hipError_t launch_decode_advance(const AdvanceArgs &a, hipStream_t stream);
+
 struct DecodeArgs {
   const void *k_layer;        // first element of layer layer_id
   const void *v_layer;

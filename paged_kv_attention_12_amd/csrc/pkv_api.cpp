@@ -395,6 +395,26 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
                                 workspace, ws_bytes, out, stream);
 }
 
+pkv_status pkv_decode_advance(const pkv_pool *pool, int32_t batch, const int32_t *req_pool_indices,
+                              int32_t *seq_lens, int32_t *kv_indptr, int32_t *out_cache_loc,
+                              int32_t *position_ids, void *stream) {
+  pkv_status st = check_pool(pool, 0);
+  if (st != PKV_OK) return st;
+  if (batch < 0) return PKV_ERR_SHAPE;
+  if (batch == 0) return PKV_OK;
+  if (!req_pool_indices || !seq_lens || !out_cache_loc) return PKV_ERR_NULL;
+  pkv::AdvanceArgs a;
+  a.req_to_token = pool->req_to_token;
+  a.max_ctx_len = pool->max_ctx_len;
+  a.req_pool_indices = req_pool_indices;
+  a.seq_lens = seq_lens;
+  a.kv_indptr = kv_indptr;
+  a.out_cache_loc = out_cache_loc;
+  a.position_ids = position_ids;
+  a.batch = batch;
+  return hip_status(pkv::launch_decode_advance(a, (hipStream_t)stream));
+}
+
 pkv_status pkv_rope_kv_store(const pkv_pool *pool, int32_t layer_id, const void *q, void *q_out,
                              int32_t n_heads, const void *k_new, const void *v_new,
                              const int32_t *position_ids, const float *freqs_cis,

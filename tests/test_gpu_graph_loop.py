@@ -2,8 +2,8 @@
 with the step metadata advanced in place on the device between replays
 (seq_lens, position_ids, out_cache_loc).  The captured work is the rotary
 embedding fused with the K/V write, the split attention and the merge; the
-metadata advance is captured too.  Every replay is checked against the oracle
-run on the same inputs."""
+metadata advance (pkv_decode_advance) is captured too.  Every replay is
+checked against the oracle run on the same inputs."""
 
 import numpy as np
 import pytest
@@ -39,8 +39,6 @@ def test_graph_captured_decode_loop_advances_metadata_in_place():
     out = torch.empty_like(q)
     ns = 8
     ws = api.decode_workspace(B_, H, d, ns)
-    table_dev = t["req_to_token"].long()
-    rows = step.req_pool_indices.long()
 
     def one_step():
         api.rope_kv_store(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, step, q, k_new,
@@ -48,13 +46,8 @@ def test_graph_captured_decode_loop_advances_metadata_in_place():
         api.decode_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, step, q_rot, None,
                         None, case.sm_scale, num_splits=ns, workspace=ws, out=out, write_kv=False)
 
-    width = case.max_ctx_len
-
     def advance():
-        step.seq_lens.add_(1)
-        step.position_ids.add_(1)
-        col = (step.seq_lens - 1).long().clamp_(0, width - 1)   # stays inside the table row
-        step.out_cache_loc.copy_(table_dev[rows, col].int())
+        api.advance_decode(t["k_buffer"], t["v_buffer"], t["req_to_token"], step)
 
     # capture on a side stream (nothing runs while capturing)
     q.zero_(), k_new.zero_(), v_new.zero_()
@@ -89,3 +82,21 @@ def test_graph_captured_decode_loop_advances_metadata_in_place():
         ref = oracle.decode(kb, vb, 0, case.req_to_token, rpi, pos + 1, q_ref, case.sm_scale)
         assert_close(to_np(out), ref, "bf16", f"graph loop step {k}")
         assert step.seq_lens.cpu().numpy().tolist() == (pos + 2).tolist()
+
+
+def test_decode_advance_matches_the_next_steps_metadata():
+    """pkv_decode_advance against the oracle's metadata of the next steps:
+    seq_lens, position_ids, out_cache_loc and kv_indptr, bit for bit."""
+    start = np.array([5, 1, 90, 33], dtype=np.int32)
+    case = W.random_case(962, list(start + 5), n_heads=4, n_kv_heads=2, head_dim=64, dtype="bf16")
+    t = W.make_tensors(case, device="cuda", poison=False)
+    step = api.DeviceStep(case.req_pool_indices, start, case.req_to_token,
+                          max_len=int((start + 5).max()))
+    for k in range(1, 5):
+        api.advance_decode(t["k_buffer"], t["v_buffer"], t["req_to_token"], step)
+        torch.cuda.synchronize()
+        md = oracle.build_step(case.req_pool_indices, start + k, case.req_to_token)
+        assert step.seq_lens.cpu().numpy().tolist() == (start + k).tolist()
+        assert np.array_equal(step.kv_indptr.cpu().numpy(), md["kv_indptr"])
+        assert np.array_equal(step.out_cache_loc.cpu().numpy(), md["out_cache_loc"])
+        assert np.array_equal(step.position_ids.cpu().numpy(), md["position_ids"])

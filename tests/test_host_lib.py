@@ -316,3 +316,16 @@ def test_rope_kv_store_argument_errors(lib):
     assert call(n=-1) == B.PKV_ERR_SHAPE
     assert call(pool=_fake_pool(head_dim=96)) == B.PKV_ERR_UNSUPPORTED
     assert call(n=0) == B.PKV_OK                      # empty step: nothing to do
+
+
+def test_decode_advance_argument_errors(lib):
+    """Host checks of pkv_decode_advance; nothing reaches the device."""
+    p = _fake_pool()
+    fake = C.c_void_p(0x4000)
+    call = lambda n=2, rpi=fake, sl=fake, loc=fake: \
+        lib.pkv_decode_advance(C.byref(p), n, rpi, sl, None, loc, None, None)
+    assert call(rpi=None) == B.PKV_ERR_NULL
+    assert call(sl=None) == B.PKV_ERR_NULL
+    assert call(loc=None) == B.PKV_ERR_NULL
+    assert call(n=-1) == B.PKV_ERR_SHAPE
+    assert call(n=0) == B.PKV_OK
