@@ -25,3 +25,4 @@ from .attention import (  # noqa: F401
     validate_step,
 )
 from .rope import round_to_bf16, rope_kv_store, rope_rotate, to_dtype  # noqa: F401
+from . import pages  # noqa: F401,E402  (pools of page_size > 1 tokens)

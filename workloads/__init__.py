@@ -43,6 +43,11 @@ class Case:
     k_scale: float = 1.0
     poison_slot: Optional[int] = None
     notes: Dict[str, object] = field(default_factory=dict)
+    # Tokens per page.  1: req_to_token holds slots.  >1: req_to_token is the
+    # page table [num_reqs, max_pages] of physical page ids, the pool holds
+    # size / page_size pages, and poison_slot is unused (poison_page instead).
+    page_size: int = 1
+    poison_page: Optional[int] = None
 
     @property
     def batch(self) -> int:
@@ -54,7 +59,7 @@ class Case:
 
     @property
     def max_ctx_len(self) -> int:
-        return int(self.req_to_token.shape[1])
+        return int(self.req_to_token.shape[1]) * self.page_size
 
     @property
     def is_decode(self) -> bool:
@@ -64,8 +69,18 @@ class Case:
     def sm_scale(self) -> float:
         return float(np.float32(1.0 / np.sqrt(self.head_dim)))
 
+    def referenced_pages(self) -> np.ndarray:
+        """Paged pools: sorted unique physical pages some request reads."""
+        ps = self.page_size
+        parts = [self.req_to_token[int(r), : (int(L) + ps - 1) // ps]
+                 for r, L in zip(self.req_pool_indices, self.seq_lens)]
+        if not parts:
+            return np.zeros(0, dtype=np.int64)
+        return np.unique(np.concatenate(parts).astype(np.int64))
+
     def referenced_slots(self) -> np.ndarray:
         """Sorted unique slots that some request reads (positions < seq_len)."""
+        assert self.page_size == 1, "slot table only"
         parts = [self.req_to_token[int(r), : int(L)]
                  for r, L in zip(self.req_pool_indices, self.seq_lens)]
         if not parts:
@@ -115,6 +130,53 @@ def random_case(seed: int, seq_lens: Sequence[int], q_lens: Optional[Sequence[in
                 head_dim=head_dim, n_layers=n_layers, layer_id=layer_id, size=size,
                 req_to_token=table, req_pool_indices=rows, seq_lens=seq_lens,
                 q_lens=q_lens, seed=seed, k_scale=k_scale, poison_slot=poison)
+
+
+def random_paged_case(seed: int, seq_lens: Sequence[int], page_size: int,
+                      q_lens: Optional[Sequence[int]] = None, n_heads: int = 4,
+                      n_kv_heads: int = 2, head_dim: int = 64, dtype: str = "f32",
+                      n_pages: Optional[int] = None, n_layers: int = 1, layer_id: int = 0,
+                      num_reqs: Optional[int] = None, max_pages: Optional[int] = None,
+                      shared_pages: int = 0, k_scale: float = 1.0,
+                      name: str = "random_paged") -> Case:
+    """Requests with the given lengths on a pool of n_pages pages of page_size
+    tokens.  Each request's logical pages map to distinct physical pages taken
+    in order from one random permutation of the pages, except that the first
+    shared_pages logical pages of every request map to the same physical pages
+    (a shared prefix; each request must be longer than that prefix so its new
+    tokens stay on private pages).  Request rows are a random subset of
+    num_reqs table rows; unused table entries point at a reserved poison
+    page."""
+    rng = np.random.default_rng(seed)
+    B = len(seq_lens)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    q_lens = np.ones(B, dtype=np.int32) if q_lens is None else np.asarray(q_lens, dtype=np.int32)
+    need = [-(-int(L) // page_size) for L in seq_lens]
+    assert all(int(L) - int(ql) >= shared_pages * page_size for L, ql in zip(seq_lens, q_lens)), \
+        "new tokens must not land on shared pages"
+    total = shared_pages + sum(n - shared_pages for n in need)
+    if n_pages is None:
+        n_pages = total + 4
+    if num_reqs is None:
+        num_reqs = B + 2
+    if max_pages is None:
+        max_pages = max(need + [1])
+    assert n_pages >= total + 1, "pool too small for distinct pages plus a poison page"
+    perm = rng.permutation(n_pages).astype(np.int32)
+    poison = int(perm[total])
+    table = _table(num_reqs, max_pages, poison)
+    rows = rng.permutation(num_reqs)[:B].astype(np.int32)
+    off = shared_pages
+    for b in range(B):
+        n = need[b]
+        table[rows[b], :shared_pages] = perm[:shared_pages]
+        table[rows[b], shared_pages:n] = perm[off:off + n - shared_pages]
+        off += n - shared_pages
+    return Case(name=name, dtype=dtype, n_heads=n_heads, n_kv_heads=n_kv_heads,
+                head_dim=head_dim, n_layers=n_layers, layer_id=layer_id,
+                size=n_pages * page_size, req_to_token=table, req_pool_indices=rows,
+                seq_lens=seq_lens, q_lens=q_lens, seed=seed, k_scale=k_scale,
+                page_size=page_size, poison_page=poison)
 
 
 def contiguous_case(seed: int, seq_lens: Sequence[int], max_seq_len: int, **kw) -> Case:
@@ -283,7 +345,25 @@ def make_tensors(case: Case, device="cpu", poison: bool = True) -> Dict[str, obj
         vb.fill_(float("nan"))
     _fill_normal(kb[case.layer_id], gen, case.k_scale)
     _fill_normal(vb[case.layer_id], gen, 1.0)
-    if poison:
+    if poison and case.page_size > 1:
+        # Page view [n_pages, page_size, Hk, d] of the attended layer: NaN in
+        # every page no request reads and in the unused tail of each
+        # request's last page.
+        ps = case.page_size
+        kv5 = [x[case.layer_id].view(case.size // ps, ps, case.n_kv_heads, case.head_dim)
+               for x in (kb, vb)]
+        keep = torch.zeros(case.size // ps, dtype=torch.bool)
+        keep[torch.from_numpy(case.referenced_pages())] = True
+        drop = (~keep).nonzero().view(-1).to(device)
+        for x in kv5:
+            x.index_fill_(0, drop, float("nan"))
+        for r, L in zip(case.req_pool_indices, case.seq_lens):
+            used = int(L) % ps
+            if used:
+                last = int(case.req_to_token[int(r), (int(L) - 1) // ps])
+                for x in kv5:
+                    x[last, used:] = float("nan")
+    elif poison:
         ref = case.referenced_slots()
         if ref.size < case.size:
             keep = torch.zeros(case.size, dtype=torch.bool)
