@@ -1,11 +1,15 @@
 /*
  * pkv.h -- C ABI of libpkv: attention over a flat, slot-addressed KV pool
- * (page_size = 1) on AMD Instinct MI355X (gfx950).
+ * (one-token pages, or pages of a power-of-two token count) on AMD Instinct
+ * MI355X (gfx950).
  *
  * Data model (AstrAI "Inference" guide, section "KVCache System"):
  *   k_buffer, v_buffer   [n_layers, size, n_kv_heads, head_dim], one dtype
  *   req_to_token         int32 [num_reqs, max_ctx_len]: logical position ->
- *                        physical slot of the pool (one-token pages)
+ *                        physical slot of the pool (one-token pages), or,
+ *                        for pools of page_size > 1 tokens per page, int32
+ *                        [num_reqs, ceil(max_ctx_len / page_size)]: logical
+ *                        page -> physical page (see pkv_pool)
  *   per step             req_pool_indices[B], seq_lens[B], kv_indptr[B+1],
  *                        qo_indptr[B+1], out_cache_loc[n_new], host max_len
  * Cached keys are already rotated: RoPE happens before the cache write
@@ -27,7 +31,8 @@
  *     a host copy of it first.
  *   - Offsets into the pool are computed in 64-bit arithmetic.
  *   - Supported: head_dim 64 or 128; dtype f32 or bf16 (prefill: bf16 only);
- *     n_heads a multiple of n_kv_heads.
+ *     n_heads a multiple of n_kv_heads; page_size 1 or a power of two up to
+ *     65536.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -52,18 +57,34 @@ typedef enum {
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 
-/* KVStorage + ReqToTokenPool ("Inference" guide, section "KVCache System"). */
+/* KVStorage + ReqToTokenPool ("Inference" guide, section "KVCache System").
+ *
+ * Pages.  The same section runs the pool in paged mode with page_size 1 or
+ * larger; the PagedCache of the v1.3.3 -> v1.3.4 compare page stores its
+ * caches as [n_layers, n_pages, page_size, n_kv_heads, head_dim] and puts
+ * logical position j of a request at offset j % page_size of the physical
+ * page that its page table lists for logical page j / page_size.  Here the
+ * flat buffer [n_layers, size, ...] is that page view with
+ * size = n_pages * page_size, so position j of the request on table row r
+ * lives in slot
+ *     req_to_token[r, j / page_size] * page_size + j % page_size,
+ * and out_cache_loc keeps naming flat slots.  page_size 0 or 1: one-token
+ * pages, req_to_token holds slots (the formula with page_size 1).
+ * page_size > 1 must be a power of two (<= 65536) dividing size; then
+ * req_to_token is [num_reqs, ceil(max_ctx_len / page_size)] of page ids. */
 typedef struct {
   void *k_buffer;               /* device, [n_layers, size, n_kv_heads, head_dim] */
   void *v_buffer;               /* device, same shape and dtype                   */
-  const int32_t *req_to_token;  /* device, [num_reqs, max_ctx_len], row-major     */
+  const int32_t *req_to_token;  /* device, [num_reqs, ceil(max_ctx_len / page_size)],
+                                   row-major: slots (page_size 1) or page ids     */
   int64_t n_layers;
-  int64_t size;                 /* slots per layer                                */
+  int64_t size;                 /* slots per layer (a multiple of page_size)      */
   int64_t num_reqs;
-  int64_t max_ctx_len;
+  int64_t max_ctx_len;          /* logical positions a table row can address      */
   int32_t n_kv_heads;
   int32_t head_dim;
   pkv_dtype dtype;
+  int32_t page_size;            /* tokens per page; 0 and 1 both mean one token   */
 } pkv_pool;
 
 /* One step's KVCache metadata (same section).  Arrays are device pointers;
@@ -103,9 +124,11 @@ int32_t pkv_last_hip_error(void);
  * All pointers are HOST memory.  Inputs: batch requests with table rows
  * req_pool_indices, context lengths seq_lens (this step's tokens included)
  * and new-token counts q_lens (NULL means 1 each, i.e. decode); the host
- * copy of req_to_token [num_reqs, max_ctx_len].  Request b's new tokens are
- * its last q_len_b logical positions, so its t-th new token is written to
- * req_to_token[r_b, seq_len_b - q_len_b + t].
+ * copy of req_to_token (rows of ceil(max_ctx_len / page_size) entries;
+ * page_size as in pkv_pool, 0 meaning 1).  Request b's new tokens are its
+ * last q_len_b logical positions, so its t-th new token is written to the
+ * slot of position seq_len_b - q_len_b + t (pkv_pool's formula).
+ * PKV_ERR_SHAPE when page_size is not 0, 1 or a power of two <= 65536.
  * Outputs: kv_indptr[batch+1], qo_indptr[batch+1], out_cache_loc (capacity
  * out_cache_loc_cap entries, filled in qo order), *n_new, *max_len,
  * *max_q_len, and, when prefill_order is not NULL, prefill_order[batch]: the
@@ -118,7 +141,7 @@ int32_t pkv_last_hip_error(void);
 pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices,
                           const int32_t *seq_lens, const int32_t *q_lens,
                           const int32_t *req_to_token, int64_t num_reqs,
-                          int64_t max_ctx_len, int32_t *kv_indptr,
+                          int64_t max_ctx_len, int32_t page_size, int32_t *kv_indptr,
                           int32_t *qo_indptr, int32_t *out_cache_loc,
                           int64_t out_cache_loc_cap, int64_t *n_new,
                           int32_t *max_len, int32_t *max_q_len, int32_t *prefill_order);
@@ -139,13 +162,15 @@ pkv_status pkv_build_positions(int32_t batch, const int32_t *seq_lens, const int
  * of `size` slots.  Accepts (PKV_OK) iff every request row is in
  * [0, num_reqs), every seq_len in [1, max_ctx_len], every q_len in
  * [0, seq_len], kv_indptr / qo_indptr are the exclusive prefix sums of the
- * lengths (qo_indptr NULL means decode: q_len 1 each), every slot read
- * (req_to_token[r_b, 0 .. seq_len_b-1]) lies in [0, size), the write slots
- * are pairwise distinct, in [0, size), and equal the table entry of their
- * token's logical position, and prefill_order (NULL: not checked) is a
- * permutation of 0..batch-1.  Else PKV_ERR_BAD_METADATA. */
+ * lengths (qo_indptr NULL means decode: q_len 1 each), every slot read (of
+ * positions 0 .. seq_len_b-1) lies in [0, size) (with pages: every page id
+ * read lies in [0, size / page_size)), the write slots are pairwise
+ * distinct, in [0, size), and equal the slot of their token's logical
+ * position, and prefill_order (NULL: not checked) is a permutation of
+ * 0..batch-1.  Else PKV_ERR_BAD_METADATA.  page_size as in pkv_pool
+ * (PKV_ERR_SHAPE when invalid or not dividing size). */
 pkv_status pkv_validate_step(int64_t size, int64_t num_reqs, int64_t max_ctx_len,
-                             const int32_t *req_to_token, int32_t batch,
+                             int32_t page_size, const int32_t *req_to_token, int32_t batch,
                              const int32_t *req_pool_indices, const int32_t *seq_lens,
                              const int32_t *kv_indptr, const int32_t *qo_indptr,
                              const int32_t *out_cache_loc, int64_t n_new,
@@ -196,7 +221,8 @@ int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_head
  * Split-KV paged decode ("Inference" guide, section "KV Cache": the single
  * new query row of each request attends over all its cached keys,
  * o = sum_j softmax(q . k_j * sm_scale) v_j; section "Attention Backend":
- * req_to_token is the page table with one-token pages and the kernel gathers
+ * req_to_token is the page table (one-token pages there; any page_size of
+ * pkv_pool here) and the kernel gathers
  * K/V itself; commit history of tests/inference/test_cache.py: per-split
  * partial outputs in a caller-owned workspace).
  *
@@ -231,7 +257,8 @@ pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_d
  * seq_lens and kv_indptr is updated in place from step to step instead of
  * being rebuilt, so that a captured graph can be replayed).  One launch:
  *   seq_lens[b] += 1; position_ids[b] = seq_lens[b] - 1 (if not NULL);
- *   out_cache_loc[b] = req_to_token[req_pool_indices[b], seq_lens[b] - 1];
+ *   out_cache_loc[b] = slot of position seq_lens[b] - 1 of table row
+ *                      req_pool_indices[b] (pkv_pool's formula);
  *   kv_indptr[b] += b for b in [0, batch] (if not NULL).
  * All arrays are device int32 owned by the caller; the caller keeps every
  * length within max_ctx_len (a position past the row reads the row's last

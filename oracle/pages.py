@@ -196,6 +196,30 @@ def prefill(k_buffer, v_buffer, layer_id, page_table, page_size, req_pool_indice
     return out
 
 
+def prefill_rows(k_buffer, v_buffer, layer_id, page_table, page_size, req_pool_indices,
+                 seq_lens, qo_indptr, q, sm_scale, rows: Iterable[Tuple[int, int]],
+                 causal: bool = True) -> np.ndarray:
+    """prefill() at the listed (token, head) rows only; token indexes the packed
+    [n_new, H, d] query.  Returns [n_rows, d]."""
+    q = _f64(q)
+    H = q.shape[1]
+    G = H // k_buffer.shape[2]
+    k5 = page_view(k_buffer, page_size)
+    v5 = page_view(v_buffer, page_size)
+    qo = [int(x) for x in qo_indptr]
+    out = []
+    for tok, h in rows:
+        i = int(np.searchsorted(qo, tok, side="right")) - 1
+        row = page_table[int(req_pool_indices[i])]
+        L = int(seq_lens[i])
+        t = tok - qo[i]
+        nk = (L - (qo[i + 1] - qo[i]) + t + 1) if causal else L
+        K = gather_rows(k5, layer_id, row, nk, h // G)
+        V = gather_rows(v5, layer_id, row, nk, h // G)
+        out.append(attend(q[tok, h], K, V, sm_scale)[0])
+    return np.stack(out) if out else np.zeros((0, q.shape[2]))
+
+
 def validate_step(size: int, page_size: int, page_table: np.ndarray, req_pool_indices,
                   seq_lens, qo_indptr, out_cache_loc) -> Tuple[bool, str]:
     """Checked mode for a paged pool: every page a request reads is a physical

@@ -17,10 +17,11 @@ class DeviceStep:
     request rows and lengths), with the host scalars kept alongside."""
 
     def __init__(self, req_pool_indices, seq_lens, req_to_token_host, q_lens=None,
-                 device="cuda", max_len: Optional[int] = None):
+                 device="cuda", max_len: Optional[int] = None, page_size: int = 1):
         import torch
-        md = B.pkv_build_step(req_pool_indices, seq_lens, req_to_token_host, q_lens)
+        md = B.pkv_build_step(req_pool_indices, seq_lens, req_to_token_host, q_lens, page_size)
         self.host = md
+        self.page_size = int(page_size)   # req_to_token is a page table when > 1
         self.batch = len(md["kv_indptr"]) - 1
         self.n_new = md["n_new"]
         # decode: a larger bound lets graph replays grow seq_lens in place
@@ -67,9 +68,9 @@ def decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceSte
         out = torch.empty_like(q)
     if write_kv:
         B.pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id, k_new, v_new,
-                       step.out_cache_loc)
+                       step.out_cache_loc, page_size=step.page_size)
     B.pkv_paged_decode(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, sm_scale,
-                       num_splits, workspace)
+                       num_splits, workspace, page_size=step.page_size)
     B.pkv_paged_decode_merge(step.batch, H, d, num_splits, workspace, out)
     return out
 
@@ -97,7 +98,8 @@ def fused_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: Dev
     if out is None:
         out = torch.empty_like(q)
     B.pkv_paged_decode_step(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, k_new, v_new,
-                            sm_scale, num_splits, workspace, sync, out)
+                            sm_scale, num_splits, workspace, sync, out,
+                            page_size=step.page_size)
     return out
 
 
@@ -117,7 +119,7 @@ def stored_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: De
     if out is None:
         out = torch.empty_like(q)
     B.pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, k_new, v_new,
-                             sm_scale, num_splits, workspace, out)
+                             sm_scale, num_splits, workspace, out, page_size=step.page_size)
     return out
 
 
@@ -126,7 +128,8 @@ def advance_decode(k_buffer, v_buffer, req_to_token, step: DeviceStep) -> None:
     launch; graph-capturable).  step.max_len must already bound the lengths
     the coming steps reach (DeviceStep(..., max_len=...))."""
     B.pkv_decode_advance(k_buffer, v_buffer, req_to_token, step.req_pool_indices, step.seq_lens,
-                         step.kv_indptr, step.out_cache_loc, step.position_ids)
+                         step.kv_indptr, step.out_cache_loc, step.position_ids,
+                         page_size=step.page_size)
 
 
 def rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q, k_new,
@@ -139,7 +142,8 @@ def rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceS
     if q_out is None:
         q_out = torch.empty_like(q)
     B.pkv_rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id, q, q_out, k_new, v_new,
-                        step.position_ids, freqs_cis, step.out_cache_loc)
+                        step.position_ids, freqs_cis, step.out_cache_loc,
+                        page_size=step.page_size)
     return q_out
 
 
@@ -151,7 +155,7 @@ def prefill_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceSt
         out = torch.empty_like(q)
     if write_kv:
         B.pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id, k_new, v_new,
-                       step.out_cache_loc)
+                       step.out_cache_loc, page_size=step.page_size)
     B.pkv_paged_prefill(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, sm_scale,
-                        causal, out)
+                        causal, out, page_size=step.page_size)
     return out

@@ -49,7 +49,7 @@ class pkv_pool(C.Structure):
         ("k_buffer", C.c_void_p), ("v_buffer", C.c_void_p), ("req_to_token", C.c_void_p),
         ("n_layers", C.c_int64), ("size", C.c_int64), ("num_reqs", C.c_int64),
         ("max_ctx_len", C.c_int64), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
-        ("dtype", C.c_int32),
+        ("dtype", C.c_int32), ("page_size", C.c_int32),
     ]
 
 
@@ -87,8 +87,8 @@ def load() -> C.CDLL:
     sig = {
         "pkv_status_string": (C.c_char_p, [C.c_int]),
         "pkv_last_hip_error": (i32, []),
-        "pkv_build_step": (C.c_int, [i32, P, P, P, P, i64, i64, P, P, P, i64, P, P, P, P]),
-        "pkv_validate_step": (C.c_int, [i64, i64, i64, P, i32, P, P, P, P, P, i64, P]),
+        "pkv_build_step": (C.c_int, [i32, P, P, P, P, i64, i64, i32, P, P, P, i64, P, P, P, P]),
+        "pkv_validate_step": (C.c_int, [i64, i64, i64, i32, P, i32, P, P, P, P, P, i64, P]),
         "pkv_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, P, i64, P]),
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "pkv_decode_pick_splits": (i32, [i32, i32, i32, i32, i64, i32]),
@@ -172,9 +172,11 @@ def dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def make_pool(k_buffer, v_buffer, req_to_token) -> pkv_pool:
+def make_pool(k_buffer, v_buffer, req_to_token, page_size: int = 1) -> pkv_pool:
     """pkv_pool view of device tensors k_buffer / v_buffer [n_layers, size,
-    n_kv_heads, head_dim] and req_to_token int32 [num_reqs, max_ctx_len]."""
+    n_kv_heads, head_dim] and req_to_token int32 [num_reqs, entries]: slots
+    (page_size 1, max_ctx_len = entries) or physical page ids of pages of
+    page_size tokens (max_ctx_len = entries * page_size)."""
     import torch
     if k_buffer.shape != v_buffer.shape or k_buffer.dtype != v_buffer.dtype:
         raise ValueError("k_buffer and v_buffer differ in shape or dtype")
@@ -185,7 +187,9 @@ def make_pool(k_buffer, v_buffer, req_to_token) -> pkv_pool:
     p.v_buffer = _dev_ptr(v_buffer, "v_buffer")
     p.req_to_token = _dev_ptr(req_to_token, "req_to_token", torch.int32)
     p.n_layers, p.size, p.n_kv_heads, p.head_dim = (int(s) for s in k_buffer.shape)
-    p.num_reqs, p.max_ctx_len = (int(s) for s in req_to_token.shape)
+    p.num_reqs = int(req_to_token.shape[0])
+    p.max_ctx_len = int(req_to_token.shape[1]) * max(int(page_size), 1)
+    p.page_size = int(page_size)
     p.dtype = dtype_code(k_buffer)
     return p
 
@@ -212,9 +216,11 @@ def make_step(batch: int, req_pool_indices, seq_lens, kv_indptr=None, qo_indptr=
 # ---------------------------------------------------------------------------
 # entry points (C names)
 # ---------------------------------------------------------------------------
-def pkv_build_step(req_pool_indices, seq_lens, req_to_token, q_lens=None) -> dict:
+def pkv_build_step(req_pool_indices, seq_lens, req_to_token, q_lens=None,
+                   page_size: int = 1) -> dict:
     """Host step metadata: returns dict of int32 numpy arrays kv_indptr,
-    qo_indptr, out_cache_loc and ints n_new, max_len, max_q_len."""
+    qo_indptr, out_cache_loc and ints n_new, max_len, max_q_len.  With
+    page_size > 1, req_to_token is the page table."""
     rpi = _host_i32(req_pool_indices, "req_pool_indices")
     sl = _host_i32(seq_lens, "seq_lens")
     ql = _host_i32(q_lens, "q_lens")
@@ -230,8 +236,9 @@ def pkv_build_step(req_pool_indices, seq_lens, req_to_token, q_lens=None) -> dic
     loc = np.zeros(max(cap, 1), dtype=np.int32)
     order = np.zeros(max(B, 1), dtype=np.int32)
     n_new, ml, mq = C.c_int64(0), C.c_int32(0), C.c_int32(0)
+    ps = int(page_size)
     st = load().pkv_build_step(B, _hp(rpi), _hp(sl), _hp(ql), _hp(table), table.shape[0],
-                               table.shape[1], _hp(kv), _hp(qo), _hp(loc), cap,
+                               table.shape[1] * max(ps, 1), ps, _hp(kv), _hp(qo), _hp(loc), cap,
                                C.byref(n_new), C.byref(ml), C.byref(mq), _hp(order))
     _check(st, "pkv_build_step")
     return {"kv_indptr": kv, "qo_indptr": qo, "out_cache_loc": loc[:n_new.value].copy(),
@@ -255,7 +262,7 @@ def pkv_build_positions(seq_lens, q_lens=None) -> np.ndarray:
 
 
 def pkv_validate_step(size: int, req_to_token, req_pool_indices, seq_lens, kv_indptr,
-                      qo_indptr, out_cache_loc, prefill_order=None) -> int:
+                      qo_indptr, out_cache_loc, prefill_order=None, page_size: int = 1) -> int:
     """Checked mode on host copies; returns the status (0 = well formed)."""
     table = _host_i32(req_to_token, "req_to_token")
     rpi = _host_i32(req_pool_indices, "req_pool_indices")
@@ -269,15 +276,17 @@ def pkv_validate_step(size: int, req_to_token, req_pool_indices, seq_lens, kv_in
         return PKV_ERR_BAD_METADATA
     if len(rpi) != B or len(kv) != B + 1 or (qo is not None and len(qo) != B + 1):
         return PKV_ERR_BAD_METADATA
-    return int(load().pkv_validate_step(int(size), table.shape[0], table.shape[1], _hp(table),
+    ps = int(page_size)
+    return int(load().pkv_validate_step(int(size), table.shape[0], table.shape[1] * max(ps, 1), ps,
+                                        _hp(table),
                                         B, _hp(rpi), _hp(sl), _hp(kv), _hp(qo), _hp(loc),
                                         0 if loc is None else len(loc), _hp(order)))
 
 
 def pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, k_new, v_new,
-                 out_cache_loc) -> None:
+                 out_cache_loc, page_size: int = 1) -> None:
     import torch
-    pool = make_pool(k_buffer, v_buffer, req_to_token)
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
     n_new = int(out_cache_loc.numel())
     if n_new and (k_new.shape[0] != n_new or v_new.shape[0] != n_new
                   or tuple(k_new.shape[1:]) != tuple(k_buffer.shape[2:])
@@ -304,8 +313,8 @@ def pkv_decode_pick_splits(batch: int, n_kv_heads: int, n_heads: int, max_len: i
 
 
 def pkv_paged_decode(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,
-                     sm_scale: float, num_splits: int, workspace) -> None:
-    pool = make_pool(k_buffer, v_buffer, req_to_token)
+                     sm_scale: float, num_splits: int, workspace, page_size: int = 1) -> None:
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
     if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
             or q.dtype != k_buffer.dtype:
         raise ValueError("q must be [batch, n_heads, head_dim] in the pool dtype")
@@ -335,9 +344,9 @@ def pkv_decode_step_pick_splits(batch: int, n_kv_heads: int, n_heads: int, max_l
 
 def pkv_paged_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,
                           k_new, v_new, sm_scale: float, num_splits: int, workspace, sync,
-                          out) -> None:
+                          out, page_size: int = 1) -> None:
     import torch
-    pool = make_pool(k_buffer, v_buffer, req_to_token)
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
     if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
             or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q / out must be [batch, n_heads, head_dim] in the pool dtype")
@@ -355,8 +364,8 @@ def pkv_paged_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step:
 
 def pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,
                            k_new, v_new, sm_scale: float, num_splits: int, workspace,
-                           out) -> None:
-    pool = make_pool(k_buffer, v_buffer, req_to_token)
+                           out, page_size: int = 1) -> None:
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
     if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
             or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q / out must be [batch, n_heads, head_dim] in the pool dtype")
@@ -373,9 +382,9 @@ def pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id: int, step
 
 
 def pkv_rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, q, q_out, k_new, v_new,
-                      position_ids, freqs_cis, out_cache_loc) -> None:
+                      position_ids, freqs_cis, out_cache_loc, page_size: int = 1) -> None:
     import torch
-    pool = make_pool(k_buffer, v_buffer, req_to_token)
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
     n_new = int(k_new.shape[0])
     if q.dim() != 3 or q.shape[0] != n_new or q.shape[2] != k_buffer.shape[3] \
             or q.dtype != k_buffer.dtype or q_out.shape != q.shape or q_out.dtype != q.dtype:
@@ -398,9 +407,9 @@ def pkv_rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, q, q_out,
 
 
 def pkv_decode_advance(k_buffer, v_buffer, req_to_token, req_pool_indices, seq_lens, kv_indptr,
-                       out_cache_loc, position_ids) -> None:
+                       out_cache_loc, position_ids, page_size: int = 1) -> None:
     import torch
-    pool = make_pool(k_buffer, v_buffer, req_to_token)
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
     n = int(seq_lens.numel())
     if req_pool_indices.numel() != n or out_cache_loc.numel() != n or \
             (position_ids is not None and position_ids.numel() != n) or \
@@ -415,8 +424,8 @@ def pkv_decode_advance(k_buffer, v_buffer, req_to_token, req_pool_indices, seq_l
 
 
 def pkv_paged_prefill(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,
-                      sm_scale: float, causal: bool, out) -> None:
-    pool = make_pool(k_buffer, v_buffer, req_to_token)
+                      sm_scale: float, causal: bool, out, page_size: int = 1) -> None:
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
     if q.dim() != 3 or q.shape[0] != step.n_new or q.shape[2] != k_buffer.shape[3] \
             or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q / out must be [n_new, n_heads, head_dim] in the pool dtype")

@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
                      ((int64_t)b * a.n_heads + h0 + g) * D + part * EPL);
   }
 
-  const int32_t *table = a.req_to_token + (int64_t)pool_row * a.max_ctx_len;
+  const int32_t *table = a.req_to_token + (int64_t)pool_row * a.table_stride;
   const int64_t row_elems = (int64_t)a.n_kv_heads * D;
   const T *kbase = reinterpret_cast<const T *>(a.k_layer) + (int64_t)hk * D + part * EPL;
   const T *vbase = reinterpret_cast<const T *>(a.v_layer) + (int64_t)hk * D + part * EPL;
@@ -180,7 +180,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
   for (int r0 = start; r0 < end; r0 += kSlotTile) {
     const int r1 = min(end, r0 + kSlotTile);
     if (r0 != start) __syncthreads();  // every wave is done with the previous round
-    for (int j = r0 + (int)threadIdx.x; j < r1; j += 256) s_slot[j - r0] = table[j];
+    for (int j = r0 + (int)threadIdx.x; j < r1; j += 256)
+      s_slot[j - r0] = slot_of_pos(table, (uint32_t)j, a.page_shift);
     __syncthreads();
     if (!active) continue;
     // Two register sets: the rows of the next iteration are in flight while
@@ -391,7 +392,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
   // its SPT entries before any LDS store (one memory round trip per run).
   // The loads depend on pool_row only, not on seq_lens[b]: entries past the
   // split's end (clamped to the table row) are staged but never used.
-  const int32_t *table = a.req_to_token + (int64_t)pool_row * a.max_ctx_len;
+  const int32_t *table = a.req_to_token + (int64_t)pool_row * a.table_stride;
   constexpr int SPT = kSlotTile / 256;
   const int run_cap = min(a.chunk, kSlotTile);
   int sv[SPT];
@@ -399,7 +400,9 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
 #pragma unroll
     for (int k = 0; k < SPT; ++k)
       if (256 * k < run_cap)
-        sv[k] = table[min((int64_t)r0 + (int)threadIdx.x + 256 * k, a.max_ctx_len - 1)];
+        sv[k] = slot_of_pos(
+            table, (uint32_t)min((int64_t)r0 + (int)threadIdx.x + 256 * k, a.max_ctx_len - 1),
+            a.page_shift);
   };
   auto store_run = [&]() {
 #pragma unroll

@@ -61,6 +61,15 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Slot of logical position j of a request whose table row is `row`: with
+// pages of 2^page_shift tokens, entry j >> page_shift is the physical page and
+// the position sits at offset j mod 2^page_shift of it (page_shift 0: the row
+// holds slots).
+__device__ __forceinline__ int32_t slot_of_pos(const int32_t *row, uint32_t j, int page_shift) {
+  const uint32_t page = (uint32_t)row[j >> page_shift];
+  return (int32_t)((page << page_shift) | (j & ((1u << page_shift) - 1u)));
+}
+
 __device__ __forceinline__ uint4 load16(const void *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }

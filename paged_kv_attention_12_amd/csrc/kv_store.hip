@@ -58,7 +58,8 @@ __global__ void __launch_bounds__(256) decode_advance_kernel(const AdvanceArgs a
     a.seq_lens[b] = L;
     if (a.position_ids) a.position_ids[b] = L - 1;
     const int64_t col = min((int64_t)L - 1, a.max_ctx_len - 1);
-    a.out_cache_loc[b] = a.req_to_token[(int64_t)a.req_pool_indices[b] * a.max_ctx_len + col];
+    a.out_cache_loc[b] = slot_of_pos(a.req_to_token + (int64_t)a.req_pool_indices[b] * a.table_stride,
+                                     (uint32_t)col, a.page_shift);
   }
   if (a.kv_indptr) a.kv_indptr[b] += b;
 }

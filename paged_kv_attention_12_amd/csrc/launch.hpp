@@ -21,8 +21,10 @@ hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t stream);
 
 // In-place advance of a decode step's metadata to the next token.
 struct AdvanceArgs {
-  const int32_t *req_to_token;
-  int64_t max_ctx_len;
+  const int32_t *req_to_token;      // slot table, or page table when page_shift > 0
+  int64_t max_ctx_len;              // logical positions a table row addresses
+  int64_t table_stride;             // entries per table row: ceil(max_ctx_len / page)
+  int32_t page_shift;               // log2(tokens per page)
   const int32_t *req_pool_indices;  // [batch]
   int32_t *seq_lens;                // [batch]
   int32_t *kv_indptr;               // [batch + 1] or null
@@ -35,8 +37,10 @@ hipError_t launch_decode_advance(const AdvanceArgs &a, hipStream_t stream);
 struct DecodeArgs {
   const void *k_layer;        // first element of layer layer_id
   const void *v_layer;
-  const int32_t *req_to_token;
-  int64_t max_ctx_len;
+  const int32_t *req_to_token;      // slot table, or page table when page_shift > 0
+  int64_t max_ctx_len;              // logical positions a table row addresses
+  int64_t table_stride;             // entries per table row: ceil(max_ctx_len / page)
+  int32_t page_shift;               // log2(tokens per page)
   const int32_t *req_pool_indices;
   const int32_t *seq_lens;
   const void *q;              // [batch, n_heads, head_dim]
@@ -106,8 +110,10 @@ hipError_t launch_decode_merge(const MergeArgs &a, int dtype, int head_dim, hipS
 struct PrefillArgs {
   const void *k_layer;
   const void *v_layer;
-  const int32_t *req_to_token;
-  int64_t max_ctx_len;
+  const int32_t *req_to_token;      // slot table, or page table when page_shift > 0
+  int64_t max_ctx_len;              // logical positions a table row addresses
+  int64_t table_stride;             // entries per table row: ceil(max_ctx_len / page)
+  int32_t page_shift;               // log2(tokens per page)
   const int32_t *req_pool_indices;
   const int32_t *qo_indptr;
   const int32_t *kv_indptr;

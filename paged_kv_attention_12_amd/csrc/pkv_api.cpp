@@ -28,6 +28,20 @@ bool dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16; }
 // Token-range granularity of one split (rows per decode iteration divide it).
 constexpr int32_t kSplitAlign = 16;
 
+// log2 of a page size (0 and 1 both mean one-token pages); -1 when the size is
+// not a power of two in [1, 65536].
+int page_shift_of(int32_t page_size) {
+  if (page_size == 0) return 0;
+  for (int sh = 0; sh <= 16; ++sh)
+    if (page_size == (1 << sh)) return sh;
+  return -1;
+}
+
+// Entries per table row: one per page of up to max_ctx_len positions.
+int64_t table_stride_of(int64_t max_ctx_len, int page_shift) {
+  return (max_ctx_len + (int64_t(1) << page_shift) - 1) >> page_shift;
+}
+
 pkv_status check_pool(const pkv_pool *p, int32_t layer_id) {
   if (!p || !p->k_buffer || !p->v_buffer || !p->req_to_token) return PKV_ERR_NULL;
   if (!dtype_ok(p->dtype)) return PKV_ERR_DTYPE;
@@ -35,8 +49,20 @@ pkv_status check_pool(const pkv_pool *p, int32_t layer_id) {
       p->n_kv_heads <= 0 || p->head_dim <= 0)
     return PKV_ERR_SHAPE;
   if (p->size > INT32_MAX) return PKV_ERR_SHAPE;  // slots are int32
+  if (p->max_ctx_len > INT32_MAX) return PKV_ERR_SHAPE;  // positions are int32
+  const int sh = page_shift_of(p->page_size);
+  if (sh < 0 || p->size % (int64_t(1) << sh) != 0) return PKV_ERR_SHAPE;
   if (layer_id < 0 || layer_id >= p->n_layers) return PKV_ERR_SHAPE;
   return PKV_OK;
+}
+
+// The table fields every gathering kernel takes.
+template <class Args>
+void set_table(Args &a, const pkv_pool *p) {
+  a.req_to_token = p->req_to_token;
+  a.max_ctx_len = p->max_ctx_len;
+  a.page_shift = page_shift_of(p->page_size);
+  a.table_stride = table_stride_of(p->max_ctx_len, a.page_shift);
 }
 
 const char *layer_ptr(const void *buf, const pkv_pool *p, int32_t layer_id) {
@@ -72,10 +98,14 @@ int32_t pkv_last_hip_error(void) { return g_last_hip_error; }
 
 pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices, const int32_t *seq_lens,
                           const int32_t *q_lens, const int32_t *req_to_token, int64_t num_reqs,
-                          int64_t max_ctx_len, int32_t *kv_indptr, int32_t *qo_indptr,
+                          int64_t max_ctx_len, int32_t page_size, int32_t *kv_indptr,
+                          int32_t *qo_indptr,
                           int32_t *out_cache_loc, int64_t out_cache_loc_cap, int64_t *n_new,
                           int32_t *max_len, int32_t *max_q_len, int32_t *prefill_order) {
-  if (batch < 0) return PKV_ERR_SHAPE;
+  const int sh = page_shift_of(page_size);
+  if (batch < 0 || sh < 0) return PKV_ERR_SHAPE;
+  const int64_t stride = table_stride_of(max_ctx_len, sh);
+  const int32_t off_mask = (1 << sh) - 1;
   if (!kv_indptr || !qo_indptr || !n_new || !max_len || !max_q_len) return PKV_ERR_NULL;
   if (batch > 0 && (!req_pool_indices || !seq_lens || !req_to_token)) return PKV_ERR_NULL;
   int64_t kv = 0, qo = 0;
@@ -93,8 +123,11 @@ pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices, const 
     kv_indptr[b + 1] = (int32_t)kv;
     if (qo + ql > out_cache_loc_cap) return PKV_ERR_SHAPE;
     if (ql > 0 && !out_cache_loc) return PKV_ERR_NULL;
-    const int32_t *row = req_to_token + r * max_ctx_len;
-    for (int32_t t = 0; t < ql; ++t) out_cache_loc[qo + t] = row[L - ql + t];
+    const int32_t *row = req_to_token + r * stride;
+    for (int32_t t = 0; t < ql; ++t) {
+      const int32_t pos = L - ql + t;
+      out_cache_loc[qo + t] = (int32_t)(((uint32_t)row[pos >> sh] << sh) | (uint32_t)(pos & off_mask));
+    }
     qo += ql;
     qo_indptr[b + 1] = (int32_t)qo;
     ml = std::max(ml, L);
@@ -132,12 +165,17 @@ pkv_status pkv_build_positions(int32_t batch, const int32_t *seq_lens, const int
 }
 
 pkv_status pkv_validate_step(int64_t size, int64_t num_reqs, int64_t max_ctx_len,
-                             const int32_t *req_to_token, int32_t batch,
+                             int32_t page_size, const int32_t *req_to_token, int32_t batch,
                              const int32_t *req_pool_indices, const int32_t *seq_lens,
                              const int32_t *kv_indptr, const int32_t *qo_indptr,
                              const int32_t *out_cache_loc, int64_t n_new,
                              const int32_t *prefill_order) {
+  const int sh = page_shift_of(page_size);
   if (batch < 0 || size <= 0 || num_reqs <= 0 || max_ctx_len <= 0) return PKV_ERR_SHAPE;
+  if (sh < 0 || size % (int64_t(1) << sh) != 0) return PKV_ERR_SHAPE;
+  const int64_t stride = table_stride_of(max_ctx_len, sh);
+  const int64_t n_pages = size >> sh;
+  const int32_t off_mask = (1 << sh) - 1;
   if (batch == 0) return n_new == 0 ? PKV_OK : PKV_ERR_BAD_METADATA;
   if (!req_to_token || !req_pool_indices || !seq_lens || !kv_indptr) return PKV_ERR_NULL;
   if (n_new > 0 && !out_cache_loc) return PKV_ERR_NULL;
@@ -154,14 +192,16 @@ pkv_status pkv_validate_step(int64_t size, int64_t num_reqs, int64_t max_ctx_len
     const int64_t q0 = qo_indptr ? qo_indptr[b] : b;
     const int64_t ql = qo_indptr ? (int64_t)qo_indptr[b + 1] - qo_indptr[b] : 1;
     if (ql < 0 || ql > L || q0 + ql > n_new) return PKV_ERR_BAD_METADATA;
-    const int32_t *row = req_to_token + r * max_ctx_len;
-    for (int64_t j = 0; j < L; ++j)
-      if (row[j] < 0 || row[j] >= size) return PKV_ERR_BAD_METADATA;
+    const int32_t *row = req_to_token + r * stride;
+    for (int64_t e = 0; e < ((L + off_mask) >> sh); ++e)  // entries of positions < L
+      if (row[e] < 0 || row[e] >= n_pages) return PKV_ERR_BAD_METADATA;
     for (int64_t t = 0; t < ql; ++t) {
       const int32_t loc = out_cache_loc[q0 + t];
       if (loc < 0 || loc >= size) return PKV_ERR_BAD_METADATA;
       if (!seen.insert(loc).second) return PKV_ERR_BAD_METADATA;
-      if (loc != row[L - ql + t]) return PKV_ERR_BAD_METADATA;
+      const int32_t pos = (int32_t)(L - ql + t);
+      if (loc != (int32_t)(((uint32_t)row[pos >> sh] << sh) | (uint32_t)(pos & off_mask)))
+        return PKV_ERR_BAD_METADATA;
     }
   }
   if (prefill_order) {
@@ -249,8 +289,7 @@ pkv_status pkv_paged_decode(const pkv_pool *pool, int32_t layer_id, const pkv_st
   pkv::DecodeArgs a;
   a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
   a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
-  a.req_to_token = pool->req_to_token;
-  a.max_ctx_len = pool->max_ctx_len;
+  set_table(a, pool);
   a.req_pool_indices = step->req_pool_indices;
   a.seq_lens = step->seq_lens;
   a.q = q;
@@ -312,8 +351,7 @@ pkv_status pkv_paged_decode_step(const pkv_pool *pool, int32_t layer_id, const p
   pkv::DecodeArgs &a = sa.d;
   a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
   a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
-  a.req_to_token = pool->req_to_token;
-  a.max_ctx_len = pool->max_ctx_len;
+  set_table(a, pool);
   a.req_pool_indices = step->req_pool_indices;
   a.seq_lens = step->seq_lens;
   a.q = q;
@@ -369,8 +407,7 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
     pkv::DecodeArgs &a = sa.d;
     a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
     a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
-    a.req_to_token = pool->req_to_token;
-    a.max_ctx_len = pool->max_ctx_len;
+    set_table(a, pool);
     a.req_pool_indices = step->req_pool_indices;
     a.seq_lens = step->seq_lens;
     a.q = q;
@@ -404,8 +441,7 @@ pkv_status pkv_decode_advance(const pkv_pool *pool, int32_t batch, const int32_t
   if (batch == 0) return PKV_OK;
   if (!req_pool_indices || !seq_lens || !out_cache_loc) return PKV_ERR_NULL;
   pkv::AdvanceArgs a;
-  a.req_to_token = pool->req_to_token;
-  a.max_ctx_len = pool->max_ctx_len;
+  set_table(a, pool);
   a.req_pool_indices = req_pool_indices;
   a.seq_lens = seq_lens;
   a.kv_indptr = kv_indptr;
@@ -489,8 +525,7 @@ pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_s
   pkv::PrefillArgs a;
   a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
   a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
-  a.req_to_token = pool->req_to_token;
-  a.max_ctx_len = pool->max_ctx_len;
+  set_table(a, pool);
   a.req_pool_indices = step->req_pool_indices;
   a.qo_indptr = step->qo_indptr;
   a.kv_indptr = step->kv_indptr;

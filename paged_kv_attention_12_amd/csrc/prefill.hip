@@ -153,7 +153,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
       qf[s] = row_ok ? load16(qrow + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
   }
 
-  const int32_t *table = a.req_to_token + (int64_t)a.req_pool_indices[i] * a.max_ctx_len;
+  const int32_t *table = a.req_to_token + (int64_t)a.req_pool_indices[i] * a.table_stride;
   const uint32_t row_bytes = (uint32_t)a.n_kv_heads * D * 2;
   const char *kbase = reinterpret_cast<const char *>(a.k_layer) + (int64_t)hk * D * 2;
   const char *vbase = reinterpret_cast<const char *>(a.v_layer) + (int64_t)hk * D * 2;
@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   // past kv_end read the last valid key instead (always masked), keeping
   // every load unconditional.
   int slot[KPIECES];
-  auto slot_of = [&](int j) { return table[(uint32_t)min(j, kv_end - 1)]; };
+  auto slot_of = [&](int j) { return slot_of_pos(table, (uint32_t)min(j, kv_end - 1), a.page_shift); };
   auto load_slots = [&](int tile, int(&ks)[KPIECES]) {
     const int base = tile * BN;
 #pragma unroll

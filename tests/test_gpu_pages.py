@@ -1,0 +1,196 @@
+"""GPU parity on pools of page_size > 1 tokens: libpkv (through its C ABI)
+against the paged oracle (oracle.pages), which gathers through the 5-D page
+view [n_layers, n_pages, page_size, Hk, d] on its own host copy.
+
+Bars as for one-token pages: the K/V write and the metadata advance are
+bit-exact; attention outputs are within max-abs 1e-5 (fp32 inputs) and
+|gpu - ref| <= 2e-2 + 1e-2 |ref| (bf16 inputs).  Unread pages, the unused
+tail of every request's last page, other layers and the poison page hold NaN.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.pages as OP
+import workloads as W
+from paged_kv_attention_12_amd import api, binding as B
+from tests.gpu_util import assert_close, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    t = t.contiguous()
+    return (t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)).cpu().numpy()
+
+
+def host_layer(case, t):
+    """The oracle's copy of the attended layer (as a one-layer pool) and of the
+    step's activations, taken before any libpkv call."""
+    sl = slice(case.layer_id, case.layer_id + 1)
+    return {"k": to_np(t["k_buffer"][sl]), "v": to_np(t["v_buffer"][sl]), "q": to_np(t["q"]),
+            "k_new": to_np(t["k_new"]), "v_new": to_np(t["v_new"])}
+
+
+def oracle_written(case, h):
+    return OP.write(h["k"], h["v"], 0, case.req_to_token, case.page_size, case.req_pool_indices,
+                    case.seq_lens, case.q_lens, h["k_new"], h["v_new"])
+
+
+def step_of(case, decode=True, max_len=None):
+    return api.DeviceStep(case.req_pool_indices, case.seq_lens, case.req_to_token,
+                          None if decode else case.q_lens, max_len=max_len,
+                          page_size=case.page_size)
+
+
+def check_metadata(case, step):
+    md = OP.build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, case.page_size,
+                       case.q_lens)
+    assert np.array_equal(step.host["out_cache_loc"], md["out_cache_loc"])
+    assert np.array_equal(step.host["kv_indptr"], md["kv_indptr"])
+    assert np.array_equal(step.host["qo_indptr"], md["qo_indptr"])
+    assert B.pkv_validate_step(case.size, case.req_to_token, case.req_pool_indices,
+                               case.seq_lens, md["kv_indptr"], md["qo_indptr"],
+                               md["out_cache_loc"], page_size=case.page_size) == B.PKV_OK
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("ps,H,Hk,d,dtype,lens,num_splits", [
+    (2, 4, 2, 64, "f32", [1, 2, 3, 37], None),
+    (16, 8, 2, 128, "f32", [15, 16, 17, 100], 3),
+    (16, 32, 8, 128, "bf16", [1, 16, 17, 300, 1000], None),
+    (64, 32, 8, 128, "bf16", [63, 64, 65, 700], 5),
+    (128, 16, 2, 64, "bf16", [5, 129, 1500], None),
+    (8, 6, 6, 128, "bf16", [9, 250, 31], 7),
+], ids=["p2_f32_d64", "p16_f32_d128", "p16_bf16_llama", "p64_bf16_llama", "p128_bf16_d64",
+        "p8_bf16_mha"])
+def test_paged_decode_matches_oracle(ps, H, Hk, d, dtype, lens, num_splits):
+    case = W.random_paged_case(100 + ps + d, lens, ps, n_heads=H, n_kv_heads=Hk, head_dim=d,
+                               dtype=dtype, n_layers=2, layer_id=1)
+    say("paged decode", case.name, ps, H, Hk, d, dtype, lens, num_splits)
+    t = W.make_tensors(case, device="cuda")
+    h = host_layer(case, t)
+    step = step_of(case)
+    check_metadata(case, step)
+    out = api.decode_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], case.layer_id, step,
+                          t["q"], t["k_new"], t["v_new"], case.sm_scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    kb, vb = oracle_written(case, h)
+    ref = OP.decode(kb, vb, 0, case.req_to_token, ps, case.req_pool_indices, case.seq_lens,
+                    h["q"], case.sm_scale)
+    assert_close(to_np(out), ref, dtype, case.name)
+
+
+@pytest.mark.parametrize("ps", [16, 64])
+def test_paged_stored_and_fused_steps_match_oracle_and_write(ps):
+    lens = [ps + 1, 3 * ps, 2000, 77]
+    case = W.random_paged_case(200 + ps, lens, ps, n_heads=32, n_kv_heads=8, head_dim=128,
+                               dtype="bf16", shared_pages=1)
+    say("paged stored/fused step", ps, lens)
+    ref_out = None
+    for kind in ("stored", "fused"):
+        t = W.make_tensors(case, device="cuda")
+        h = host_layer(case, t)
+        step = step_of(case)
+        fn = api.stored_decode_step if kind == "stored" else api.fused_decode_step
+        out = fn(t["k_buffer"], t["v_buffer"], t["req_to_token"], case.layer_id, step, t["q"],
+                 t["k_new"], t["v_new"], case.sm_scale)
+        torch.cuda.synchronize()
+        kb, vb = oracle_written(case, h)
+        if ref_out is None:
+            ref_out = OP.decode(kb, vb, 0, case.req_to_token, ps, case.req_pool_indices,
+                                case.seq_lens, h["q"], case.sm_scale)
+        assert_close(to_np(out), ref_out, "bf16", kind)
+        # the pool holds exactly the oracle's write (the upcast to float is
+        # exact, so equal floats are equal values; NaN poison must stay NaN)
+        got_k = to_np(t["k_buffer"][case.layer_id])
+        got_v = to_np(t["v_buffer"][case.layer_id])
+        assert np.array_equal(got_k, kb[0], equal_nan=True), kind
+        assert np.array_equal(got_v, vb[0], equal_nan=True), kind
+
+
+def test_paged_llama_b1_long_context_sampled():
+    case = W.llama_b1_decode_paged(32768, page_size=64)
+    say("paged llama b1", case.name)
+    t = W.make_tensors(case, device="cuda")
+    h = host_layer(case, t)
+    step = step_of(case)
+    out = api.stored_decode_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], case.layer_id,
+                                 step, t["q"], t["k_new"], t["v_new"], case.sm_scale)
+    torch.cuda.synchronize()
+    kb, vb = oracle_written(case, h)
+    pairs = [(0, h_) for h_ in (0, 7, 8, 31)]
+    ref = OP.decode_pairs(kb, vb, 0, case.req_to_token, 64, case.req_pool_indices,
+                          case.seq_lens, h["q"], case.sm_scale, pairs)
+    got = to_np(out)[[b for b, _ in pairs], [h_ for _, h_ in pairs]]
+    assert_close(got, ref, "bf16", case.name)
+
+
+def test_paged_advance_matches_next_step_metadata():
+    ps = 16
+    case = W.random_paged_case(300, [5, 15, 16, 40], ps, n_heads=4, n_kv_heads=2, head_dim=64,
+                               max_pages=8)
+    say("paged advance", ps)
+    t = W.make_tensors(case, device="cuda")
+    step = step_of(case, max_len=8 * ps)
+    lens = case.seq_lens.copy()
+    for k in range(1, 4):
+        api.advance_decode(t["k_buffer"], t["v_buffer"], t["req_to_token"], step)
+        torch.cuda.synchronize()
+        md = OP.build_step(case.req_pool_indices, lens + k, case.req_to_token, ps)
+        assert np.array_equal(step.seq_lens.cpu().numpy(), lens + k)
+        assert np.array_equal(step.out_cache_loc.cpu().numpy(), md["out_cache_loc"]), k
+        assert np.array_equal(step.kv_indptr.cpu().numpy(), md["kv_indptr"]), k
+        assert np.array_equal(step.position_ids.cpu().numpy(), lens + k - 1), k
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("ps,q_lens,prefix,causal", [
+    (16, [1, 17, 64, 200], [0, 15, 33, 300], True),
+    (64, [130, 5, 1, 64], [64, 0, 700, 63], True),
+    (8, [40, 3], [9, 100], False),
+    (128, [300, 0, 129], [1, 5, 256], True),
+], ids=["p16", "p64", "p8_noncausal", "p128_empty_req"])
+def test_paged_prefill_matches_oracle(ps, q_lens, prefix, causal):
+    lens = [p + q for p, q in zip(prefix, q_lens)]
+    case = W.random_paged_case(400 + ps, lens, ps, q_lens=q_lens, n_heads=16, n_kv_heads=4,
+                               head_dim=128, dtype="bf16")
+    say("paged prefill", ps, q_lens, prefix, causal)
+    t = W.make_tensors(case, device="cuda")
+    h = host_layer(case, t)
+    step = step_of(case, decode=False)
+    check_metadata(case, step)
+    out = api.prefill_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], case.layer_id, step,
+                           t["q"], t["k_new"], t["v_new"], case.sm_scale, causal=causal)
+    torch.cuda.synchronize()
+    kb, vb = oracle_written(case, h)
+    ref = OP.prefill(kb, vb, 0, case.req_to_token, ps, case.req_pool_indices, case.seq_lens,
+                     step.host["qo_indptr"], h["q"], case.sm_scale, causal=causal)
+    assert_close(to_np(out), ref, "bf16", case.name)
+
+
+def test_paged_prefill_full_config_sampled():
+    case = W.ragged_prefill_paged(64)
+    say("paged prefill full", case.name)
+    t = W.make_tensors(case, device="cuda")
+    h = host_layer(case, t)
+    step = step_of(case, decode=False)
+    out = api.prefill_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], case.layer_id, step,
+                           t["q"], t["k_new"], t["v_new"], case.sm_scale)
+    torch.cuda.synchronize()
+    kb, vb = oracle_written(case, h)
+    qo = step.host["qo_indptr"]
+    # first, middle and last new token of the four longest requests, three heads
+    rows = []
+    for i in np.argsort(-case.seq_lens)[:4]:
+        for tok in (qo[i], (qo[i] + qo[i + 1]) // 2, qo[i + 1] - 1):
+            rows += [(int(tok), hh) for hh in (0, 13, 31)]
+    ref = OP.prefill_rows(kb, vb, 0, case.req_to_token, 64, case.req_pool_indices,
+                          case.seq_lens, qo, h["q"], case.sm_scale, rows)
+    got = to_np(out)[[r for r, _ in rows], [hh for _, hh in rows]]
+    assert_close(got, ref, "bf16", case.name)

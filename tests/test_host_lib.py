@@ -329,3 +329,81 @@ def test_decode_advance_argument_errors(lib):
     assert call(loc=None) == B.PKV_ERR_NULL
     assert call(n=-1) == B.PKV_ERR_SHAPE
     assert call(n=0) == B.PKV_OK
+
+
+# ---------------------------------------------------------------------------
+# pools of page_size > 1 tokens
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("ps", [2, 16, 64])
+def test_paged_build_step_matches_paged_oracle(lib, ps):
+    import oracle.pages as OP
+    lens = [1, ps, ps + 1, 5 * ps + 3]
+    q_lens = [1, ps, 2, 3 * ps]
+    case = W.random_paged_case(70 + ps, lens, ps, q_lens=q_lens)
+    got = B.pkv_build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, q_lens, ps)
+    ref = OP.build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, ps, q_lens)
+    for k in ("kv_indptr", "qo_indptr", "out_cache_loc"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert got["max_len"] == ref["max_len"] and got["n_new"] == ref["n_new"]
+
+
+def test_paged_golden_build_step(lib):
+    g = json.load(open(os.path.join(GOLDEN, "paged_step_metadata.json")))
+    md = B.pkv_build_step(g["req_pool_indices"], g["seq_lens"], np.array(g["page_table"]),
+                          g["q_lens"], g["page_size"])
+    assert md["out_cache_loc"].tolist() == g["out_cache_loc"]
+    assert md["kv_indptr"].tolist() == g["kv_indptr"]
+
+
+def test_paged_validate_agrees_with_paged_oracle(lib):
+    import oracle.pages as OP
+    ps = 8
+    case = W.random_paged_case(80, [7, 8, 9, 30], ps, q_lens=[7, 1, 2, 9])
+    md = OP.build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, ps, case.q_lens)
+
+    def both(table=case.req_to_token, loc=md["out_cache_loc"], size=case.size):
+        lib_ok = B.pkv_validate_step(size, table, case.req_pool_indices, case.seq_lens,
+                                     md["kv_indptr"], md["qo_indptr"], loc,
+                                     page_size=ps) == B.PKV_OK
+        ref_ok, _ = OP.validate_step(size, ps, table, case.req_pool_indices, case.seq_lens,
+                                     md["qo_indptr"], loc)
+        return lib_ok, ref_ok
+
+    assert both() == (True, True)
+    x = md["out_cache_loc"].copy(); x[0] += 1
+    assert both(loc=x) == (False, False)
+    x = md["out_cache_loc"].copy(); x[1] = x[0]
+    assert both(loc=x) == (False, False)
+    t = case.req_to_token.copy(); t[case.req_pool_indices[3], 2] = case.size // ps
+    assert both(table=t) == (False, False)
+    t = case.req_to_token.copy(); t[case.req_pool_indices[0], 0] = -1
+    assert both(table=t) == (False, False)
+
+
+def test_page_size_argument_errors(lib):
+    case = W.random_paged_case(81, [5, 9], 4)
+    for bad in (3, 6, 1 << 17, -4):
+        with pytest.raises(B.PkvError):
+            B.pkv_build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, None, bad)
+    md = B.pkv_build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, None, 4)
+    st = B.pkv_validate_step(case.size + 2, case.req_to_token, case.req_pool_indices,
+                             case.seq_lens, md["kv_indptr"], None, md["out_cache_loc"],
+                             page_size=4)
+    assert st == B.PKV_ERR_SHAPE
+
+
+def test_pool_page_size_checks_before_launch(lib):
+    """A pool whose page size is not a power of two, or does not divide the
+    slot count, is refused by every pool-taking entry point before launch."""
+    fake = C.c_void_p(0x4000)
+    s = B.pkv_step()
+    s.batch, s.req_pool_indices, s.seq_lens, s.max_len = 2, 0x10, 0x20, 8
+    for ps, size in ((3, 48), (6, 48), (1 << 17, 1 << 17), (-2, 48), (16, 40)):
+        p = _fake_pool()
+        p.page_size, p.size = ps, size
+        assert lib.pkv_kv_store(C.byref(p), 0, fake, fake, fake, 4, None) == B.PKV_ERR_SHAPE
+        assert lib.pkv_paged_decode(C.byref(p), 0, C.byref(s), fake, 8, 0.1, 1, fake, 1 << 20,
+                                    None) == B.PKV_ERR_SHAPE
+    p = _fake_pool()
+    p.page_size, p.size = 16, 48
+    assert lib.pkv_kv_store(C.byref(p), 0, fake, fake, fake, 0, None) == B.PKV_OK

@@ -283,3 +283,17 @@ _orig_write = OP.write
 def test_planted_paging_mistake_is_caught(monkeypatch, name, target, mutant):
     monkeypatch.setattr(OP, target, mutant)
     assert not _pins_hold(), name
+
+
+def test_paged_prefill_rows_sampler_matches_full():
+    ps = 4
+    case = W.random_paged_case(17, [9, 14], ps, q_lens=[4, 6], n_heads=4, n_kv_heads=2,
+                               head_dim=8)
+    t = np_tensors(case)
+    kb, vb, md = paged_store(case, t)
+    full = OP.prefill(kb, vb, 0, case.req_to_token, ps, case.req_pool_indices, case.seq_lens,
+                      md["qo_indptr"], t["q"], case.sm_scale)
+    rows = [(0, 0), (3, 3), (4, 1), (9, 2)]
+    sub = OP.prefill_rows(kb, vb, 0, case.req_to_token, ps, case.req_pool_indices, case.seq_lens,
+                          md["qo_indptr"], t["q"], case.sm_scale, rows)
+    assert np.array_equal(sub, full[[r for r, _ in rows], [h for _, h in rows]])

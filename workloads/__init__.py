@@ -289,6 +289,34 @@ def ragged_prefill(seed: int = 4, n_req: int = 16, q_hi: int = 2048, p_hi: int =
     return c
 
 
+def llama_b1_decode_paged(seq_len: int, page_size: int = 64, seed: int = 2, n_layers: int = 32,
+                          layer_id: int = 31) -> Case:
+    """The Llama-3-8B-shaped single-request decode on a pool of page_size-token
+    pages: 32 query / 8 kv heads, head_dim 128, bf16, 32 layers (layer 31
+    attended), 65536 slots = 65536 / page_size pages; the request's logical
+    pages on the first ceil(seq_len / page_size) pages of a random page
+    permutation."""
+    c = random_paged_case(seed * 100003 + seq_len, [seq_len], page_size, n_heads=32,
+                          n_kv_heads=8, head_dim=128, dtype="bf16",
+                          n_pages=65536 // page_size, n_layers=n_layers, layer_id=layer_id,
+                          num_reqs=1, name=f"llama_b1_decode_paged{page_size}_L{seq_len}")
+    return c
+
+
+def ragged_prefill_paged(page_size: int = 64, seed: int = 4, n_req: int = 16, q_hi: int = 2048,
+                         p_hi: int = 4096, size: int = 131072) -> Case:
+    """The ragged causal prefill (same length draws as ragged_prefill) on a
+    pool of page_size-token pages: 131072 slots = 131072 / page_size pages;
+    every request's logical pages on disjoint pages of one page permutation."""
+    rng = np.random.default_rng(seed)
+    q_lens = rng.integers(1, q_hi + 1, size=n_req).astype(np.int32)
+    prefix = rng.integers(0, p_hi + 1, size=n_req).astype(np.int32)
+    lens = (prefix + q_lens).astype(np.int32)
+    return random_paged_case(seed + 1, lens, page_size, q_lens=q_lens, n_heads=32, n_kv_heads=8,
+                             head_dim=128, dtype="bf16", n_pages=size // page_size,
+                             num_reqs=n_req, name=f"ragged_prefill_paged{page_size}")
+
+
 def long_context_decode(seed: int = 5, B: int = 8, seq_len: int = 131072,
                         size: int = 1 << 20, n_layers: int = 4, layer_id: int = 3) -> Case:
     """Long-context split-KV stress, bf16: 8 requests of 131072 tokens, 64 query
