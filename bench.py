@@ -67,14 +67,15 @@ class DecodeRunner:
                     W._fill_normal(t["k_buffer"][layer], g, case.k_scale)
                     W._fill_normal(t["v_buffer"][layer], g)
         self.t = t
-        self.step = api.DeviceStep(case.req_pool_indices, case.seq_lens, case.req_to_token)
+        self.step = api.DeviceStep(case.req_pool_indices, case.seq_lens, case.req_to_token,
+                                   page_size=case.page_size)
         H, d = case.n_heads, case.head_dim
         self.num_splits = num_splits or B.pkv_decode_pick_splits(
             case.batch, case.n_kv_heads, H, self.step.max_len, self.step.total_len)
         self.ws = api.decode_workspace(case.batch, H, d, self.num_splits)
         self.ws_bytes = self.ws.numel() * 4
         self.out = torch.empty_like(t["q"])
-        self.pool = B.make_pool(t["k_buffer"], t["v_buffer"], t["req_to_token"])
+        self.pool = B.make_pool(t["k_buffer"], t["v_buffer"], t["req_to_token"], case.page_size)
         self.pool_ref = C.byref(self.pool)
         self.step_ref = C.byref(self.step.c)
         self.out_dtype = B.dtype_code(self.out)
@@ -115,13 +116,19 @@ class DecodeRunner:
         return (self.case.layer_id - k) % n
 
     # ---- algorithmic work ----
+    def table_bytes(self):
+        """Table entries the step needs: one slot id per token, or one page id
+        per page of page_size tokens."""
+        ps = self.case.page_size
+        return 4 * int(sum((int(L) + ps - 1) // ps for L in self.case.seq_lens))
+
     def kernel_bytes(self):
         """Split kernel per launch: every key/value row of every request once,
-        the slot ids, and q."""
+        the table entries, and q."""
         c = self.case
         row = c.n_kv_heads * c.head_dim * 2
         L = int(c.seq_lens.sum())
-        return L * 2 * row + L * 4 + c.batch * c.n_heads * c.head_dim * 2
+        return L * 2 * row + self.table_bytes() + c.batch * c.n_heads * c.head_dim * 2
 
     def unique_kernel_bytes(self):
         c = self.case
@@ -255,16 +262,17 @@ def prefill_flops(case):
     return 4 * d * H * int(tot)
 
 
-def bench_prefill(reps=20):
+def bench_prefill(reps=20, case=None):
     import torch
     import workloads as W
     from paged_kv_attention_12_amd import api, binding as B
-    case = W.ragged_prefill()
+    case = case or W.ragged_prefill()
     t = W.make_tensors(case, device="cuda", poison=False)
-    step = api.DeviceStep(case.req_pool_indices, case.seq_lens, case.req_to_token, case.q_lens)
+    step = api.DeviceStep(case.req_pool_indices, case.seq_lens, case.req_to_token, case.q_lens,
+                          page_size=case.page_size)
     out = torch.empty_like(t["q"])
     lib = B.load()
-    pool = B.make_pool(t["k_buffer"], t["v_buffer"], t["req_to_token"])
+    pool = B.make_pool(t["k_buffer"], t["v_buffer"], t["req_to_token"], case.page_size)
     st = torch.cuda.current_stream().cuda_stream
     cur = torch.cuda.current_stream()
 
@@ -321,7 +329,8 @@ def bench_prefill(reps=20):
     med = float(np.median(t_pre))
     row = case.n_kv_heads * case.head_dim * 2
     return {
-        "workload": "ragged_causal_prefill_16req",
+        "workload": "ragged_causal_prefill_16req" + (
+            f"_pages{case.page_size}" if case.page_size > 1 else ""),
         "n_new_tokens": int(case.q_lens.sum()), "kv_tokens": int(case.seq_lens.sum()),
         "flops": flops, "prefill_ms": med * 1e3, "prefill_ms_p10_p90":
             [float(np.percentile(t_pre, 10)) * 1e3, float(np.percentile(t_pre, 90)) * 1e3],
@@ -527,6 +536,28 @@ def main():
         extra["prefill"] = bench_prefill()
         log(f"  prefill {extra['prefill']['prefill_ms']:.3f} ms "
             f"{extra['prefill']['tflops']:.1f} TFLOP/s")
+
+        # the same workloads on pools of 64-token pages
+        log("paged pools (64-token pages)")
+        rp = StoredDecodeRunner(W.llama_b1_decode_paged(L_head, page_size=64))
+        spp, ok = timed_graph(rp, 50, 5)
+        ktp = kernel_event_times(rp, 32, reps=2)
+        pre_p = bench_prefill(case=W.ragged_prefill_paged(64))
+        extra["pages64"] = {
+            "b1_decode_L32768": {
+                "step_us": spp * 1e6, "split_kernel_us": float(ktp.mean()) * 1e6,
+                "step_gbps": rp.step_bytes() / spp / 1e9,
+                "split_kernel_gbps": rp.kernel_bytes() / float(ktp.mean()) / 1e9,
+                "frac_of_hbm_peak": rp.kernel_bytes() / float(ktp.mean()) / 1e9 / HBM_PEAK_GBPS,
+                "num_splits": rp.num_splits, "graph_ok": ok},
+            "prefill": {k: pre_p[k] for k in ("workload", "flops", "prefill_ms", "tflops",
+                                              "frac_of_bf16_peak")},
+        }
+        del rp
+        torch.cuda.empty_cache()
+        log(f"  B=1 L={L_head} pages of 64: step {spp * 1e6:.1f} us, split kernel "
+            f"{ktp.mean() * 1e6:.1f} us; prefill {pre_p['prefill_ms']:.3f} ms "
+            f"{pre_p['tflops']:.1f} TFLOP/s")
 
     cpu = None
     if not args.no_cpu_baseline:
