@@ -251,6 +251,87 @@ def kernel_event_times(runner, launches, reps=3):
 
 
 # ---------------------------------------------------------------------------
+# graph-captured decode loop: one token of a 32-layer forward per replay
+# ---------------------------------------------------------------------------
+def bench_decode_loop(L, tokens=8):
+    """Per token, for every layer (31 .. 0): the rotary embedding fused with
+    the K/V write of the new token, the split attention and the merge; then
+    the in-place advance of the step metadata (seq_lens, position_ids,
+    out_cache_loc, kv_indptr).  Captured once, replayed token after token.
+    The request starts at position L - tokens - 1, so the table row (L
+    positions) covers every token and the last advance.  Also timed: the
+    same launches issued eagerly from Python through the C ABI."""
+    import torch
+    import workloads as W
+    from paged_kv_attention_12_amd import api
+    r = DecodeRunner(W.llama_b1_decode(L))
+    c = r.case
+    t = r.t
+    p0 = L - tokens - 1
+    step = api.DeviceStep(c.req_pool_indices, np.array([p0 + 1], np.int32), c.req_to_token,
+                          max_len=L)
+    freqs = W.rope_table(L, c.head_dim, device="cuda")
+    ns = r.num_splits
+    ws = api.decode_workspace(1, c.n_heads, c.head_dim, ns)
+    q_rot = torch.empty_like(t["q"])
+    out = torch.empty_like(t["q"])
+    kb, vb, tab = t["k_buffer"], t["v_buffer"], t["req_to_token"]
+
+    def one_token():
+        for layer in range(c.n_layers - 1, -1, -1):
+            api.rope_kv_store(kb, vb, tab, layer, step, t["q"], t["k_new"], t["v_new"], freqs,
+                              q_out=q_rot)
+            api.decode_step(kb, vb, tab, layer, step, q_rot, None, None, c.sm_scale,
+                            num_splits=ns, workspace=ws, out=out, write_kv=False)
+        api.advance_decode(kb, vb, tab, step)
+
+    def reset():
+        step.seq_lens.fill_(p0 + 1)
+        step.position_ids.fill_(p0)
+        step.kv_indptr[1:].fill_(p0 + 1)
+        step.out_cache_loc.fill_(int(c.req_to_token[int(c.req_pool_indices[0]), p0]))
+
+    # eager: every launch from Python
+    one_token()
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(tokens):
+        one_token()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / tokens
+    # graph: one token's launches captured once (nothing runs while capturing)
+    reset()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            one_token()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g.replay()  # warm: the first token
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(tokens):
+        g.replay()
+    torch.cuda.synchronize()
+    graph = (time.perf_counter() - t0) / tokens
+    advanced = int(step.seq_lens.item()) == p0 + 1 + tokens
+    del g, r
+    torch.cuda.empty_cache()
+    n = c.n_layers
+    return {"tokens": tokens, "layers": n, "context": [p0 + 1, p0 + tokens],
+            "graph_us_per_token": graph * 1e6, "graph_us_per_layer": graph / n * 1e6,
+            "eager_us_per_token": eager * 1e6, "eager_us_per_layer": eager / n * 1e6,
+            "metadata_advanced": advanced}
+
+
+# ---------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------
 def prefill_flops(case):
@@ -536,6 +617,12 @@ def main():
         extra["prefill"] = bench_prefill()
         log(f"  prefill {extra['prefill']['prefill_ms']:.3f} ms "
             f"{extra['prefill']['tflops']:.1f} TFLOP/s")
+
+        log("graph-captured decode loop")
+        extra["decode_loop"] = {str(L): bench_decode_loop(L) for L in (1024, 32768)}
+        for L, v in extra["decode_loop"].items():
+            log(f"  L={L}: graph {v['graph_us_per_layer']:.1f} us/layer, eager "
+                f"{v['eager_us_per_layer']:.1f} us/layer, advanced={v['metadata_advanced']}")
 
         # the same workloads on pools of 64-token pages
         log("paged pools (64-token pages)")
