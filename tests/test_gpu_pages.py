@@ -20,11 +20,6 @@ from tests.gpu_util import assert_close, say, to_np
 pytestmark = pytest.mark.gpu
 
 
-def bits(t):
-    t = t.contiguous()
-    return (t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)).cpu().numpy()
-
-
 def host_layer(case, t):
     """The oracle's copy of the attended layer (as a one-layer pool) and of the
     step's activations, taken before any libpkv call."""
