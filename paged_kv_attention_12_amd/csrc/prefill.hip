@@ -89,8 +89,9 @@ struct Smem {
 };
 
 // OFF32: every row of the layer lies within 4 GiB of the layer base, so row
-// addresses are a uniform 64-bit base plus a 32-bit byte offset.
-template <int D, bool OFF32>
+// addresses are a uniform 64-bit base plus a 32-bit byte offset.  PAGED: the
+// table holds page ids of pages of 2^page_shift tokens (else slot ids).
+template <int D, bool OFF32, bool PAGED>
 __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   constexpr int KS = Smem<D>::KS;
   constexpr int VS = Smem<D>::VS;
@@ -176,7 +177,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   // past kv_end read the last valid key instead (always masked), keeping
   // every load unconditional.
   int slot[KPIECES];
-  auto slot_of = [&](int j) { return slot_of_pos(table, (uint32_t)min(j, kv_end - 1), a.page_shift); };
+  auto slot_of = [&](int j) {
+    const uint32_t pos = (uint32_t)min(j, kv_end - 1);
+    if constexpr (PAGED)
+      return slot_of_pos(table, pos, a.page_shift);
+    else
+      return table[pos];
+  };
   auto load_slots = [&](int tile, int(&ks)[KPIECES]) {
     const int base = tile * BN;
 #pragma unroll
@@ -399,10 +406,15 @@ hipError_t launch_d(const PrefillArgs &a, bool off32, hipStream_t stream) {
   PrefillArgs args = a;
   args.row_blocks = (int32_t)row_blocks;
   const dim3 grid((uint32_t)blocks);
-  if (off32)
-    hipLaunchKernelGGL((prefill_kernel<D, true>), grid, dim3(NT), 0, stream, args);
+  const bool paged = a.page_shift > 0;
+  if (off32 && !paged)
+    hipLaunchKernelGGL((prefill_kernel<D, true, false>), grid, dim3(NT), 0, stream, args);
+  else if (off32)
+    hipLaunchKernelGGL((prefill_kernel<D, true, true>), grid, dim3(NT), 0, stream, args);
+  else if (!paged)
+    hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, dim3(NT), 0, stream, args);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, false>), grid, dim3(NT), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<D, false, true>), grid, dim3(NT), 0, stream, args);
   return hipGetLastError();
 }
 
