@@ -407,3 +407,20 @@ def test_pool_page_size_checks_before_launch(lib):
     p = _fake_pool()
     p.page_size, p.size = 16, 48
     assert lib.pkv_kv_store(C.byref(p), 0, fake, fake, fake, 0, None) == B.PKV_OK
+
+
+def test_c_caller_of_the_header(lib, tmp_path):
+    """include/pkv.h compiles as C99 with gcc and a C program linked against
+    libpkv.so gets the hand-worked step metadata (one-token and 4-token pages)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    exe = str(tmp_path / "host_abi")
+    libdir = os.path.dirname(B.lib_path())
+    src = os.path.join(ROOT, "tests", "c", "host_abi.c")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    src, "-L", libdir, "-lpkv", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
