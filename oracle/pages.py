@@ -221,19 +221,34 @@ def prefill_rows(k_buffer, v_buffer, layer_id, page_table, page_size, req_pool_i
 
 
 def validate_step(size: int, page_size: int, page_table: np.ndarray, req_pool_indices,
-                  seq_lens, qo_indptr, out_cache_loc) -> Tuple[bool, str]:
-    """Checked mode for a paged pool: every page a request reads is a physical
-    page of the pool, and each write slot is the flat slot of its token's
-    position; write slots pairwise distinct."""
-    n_pages = size // page_size
+                  seq_lens, kv_indptr, qo_indptr, out_cache_loc) -> Tuple[bool, str]:
+    """Checked mode for a paged pool ("Inference" guide, section "KVCache
+    System": kv_indptr and qo_indptr are the exclusive prefix sums of seq_lens
+    and of the new-token counts; out_cache_loc holds the write slots).  A step
+    is well formed when the pool is whole pages, every request row is a row of
+    the page table, every length is in [1, max_ctx_len] (max_ctx_len = table
+    width x page_size), both indptr arrays are those prefix sums, every
+    new-token count is in [0, seq_len], every page a request reads is a
+    physical page of the pool, and each write slot is the flat slot of its
+    token's position, the write slots pairwise distinct."""
+    B = len(seq_lens)
     if size % page_size != 0:
         return False, "pool size not whole pages"
+    n_pages = size // page_size
+    if len(req_pool_indices) != B or len(kv_indptr) != B + 1 or len(qo_indptr) != B + 1:
+        return False, "array lengths"
+    if int(kv_indptr[0]) != 0 or int(qo_indptr[0]) != 0:
+        return False, "indptr start"
+    if len(out_cache_loc) != int(qo_indptr[B]):
+        return False, "out_cache_loc length"
     seen = set()
-    for b in range(len(seq_lens)):
+    for b in range(B):
         r = int(req_pool_indices[b])
         L = int(seq_lens[b])
         if not (0 <= r < page_table.shape[0]) or not (1 <= L <= page_table.shape[1] * page_size):
             return False, f"request {b}"
+        if int(kv_indptr[b + 1]) - int(kv_indptr[b]) != L:
+            return False, f"kv_indptr {b}"
         for lp in range((L + page_size - 1) // page_size):
             if not (0 <= int(page_table[r, lp]) < n_pages):
                 return False, f"page ({b},{lp})"

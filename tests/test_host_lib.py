@@ -366,7 +366,7 @@ def test_paged_validate_agrees_with_paged_oracle(lib):
                                      md["kv_indptr"], md["qo_indptr"], loc,
                                      page_size=ps) == B.PKV_OK
         ref_ok, _ = OP.validate_step(size, ps, table, case.req_pool_indices, case.seq_lens,
-                                     md["qo_indptr"], loc)
+                                     md["kv_indptr"], md["qo_indptr"], loc)
         return lib_ok, ref_ok
 
     assert both() == (True, True)
@@ -424,3 +424,47 @@ def test_c_caller_of_the_header(lib, tmp_path):
                     src, "-L", libdir, "-lpkv", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("ps", [1, 4])
+def test_validate_step_random_corruptions_agree_with_oracle(lib, ps):
+    """Randomised agreement of the library's checked mode with the oracle's on
+    one well-formed step and many single-field corruptions of it (slot or page
+    table entries, write slots, lengths, request rows, prefix sums)."""
+    import oracle.pages as OP
+    rng = np.random.default_rng(900 + ps)
+    lens = [3, 9, 1, 14]
+    q_lens = [1, 4, 1, 6]
+    if ps == 1:
+        case = W.random_case(91, lens, q_lens)
+        md = oracle.build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, q_lens)
+    else:
+        case = W.random_paged_case(91, lens, ps, q_lens=q_lens)
+        md = OP.build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, ps, q_lens)
+    base = dict(req_to_token=case.req_to_token, req_pool_indices=case.req_pool_indices,
+                seq_lens=case.seq_lens, kv_indptr=md["kv_indptr"], qo_indptr=md["qo_indptr"],
+                out_cache_loc=md["out_cache_loc"])
+
+    def both(a):
+        lib_ok = B.pkv_validate_step(case.size, page_size=ps, **a) == B.PKV_OK
+        if ps == 1:
+            ref_ok, _ = oracle.validate_step(case.size, case.num_reqs, case.max_ctx_len, **a)
+        else:
+            ref_ok, _ = OP.validate_step(case.size, ps, a["req_to_token"], a["req_pool_indices"],
+                                         a["seq_lens"], a["kv_indptr"], a["qo_indptr"],
+                                         a["out_cache_loc"])
+        return lib_ok, ref_ok
+
+    assert both(base) == (True, True)
+    n_bad = 0
+    for _ in range(300):
+        a = {k: np.array(v, copy=True) for k, v in base.items()}
+        field = rng.choice(list(a))
+        arr = a[field]
+        flat = arr.reshape(-1)
+        i = int(rng.integers(0, flat.size))
+        flat[i] = flat[i] + int(rng.choice([-2, -1, 1, 2, 7, -100, 100000]))
+        lib_ok, ref_ok = both(a)
+        assert lib_ok == ref_ok, (field, i, flat[i])
+        n_bad += not lib_ok
+    assert n_bad > 100

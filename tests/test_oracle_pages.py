@@ -122,7 +122,8 @@ def test_write_matches_flat_kv_store_at_build_step_slots():
     assert np.array_equal(kbp, kb1, equal_nan=True) and np.array_equal(vbp, vb1, equal_nan=True)
     assert len(set(md["out_cache_loc"].tolist())) == md["n_new"]
     ok, why = OP.validate_step(case.size, 16, case.req_to_token, case.req_pool_indices,
-                               case.seq_lens, md["qo_indptr"], md["out_cache_loc"])
+                               case.seq_lens, md["kv_indptr"], md["qo_indptr"],
+                               md["out_cache_loc"])
     assert ok, why
 
 
@@ -209,18 +210,24 @@ def test_paged_validate_rejects_each_corruption():
     case = W.random_paged_case(16, [6, 9], ps, q_lens=[2, 1], n_heads=2, n_kv_heads=1, head_dim=8)
     md = OP.build_step(case.req_pool_indices, case.seq_lens, case.req_to_token, ps, case.q_lens)
     args = (case.size, ps, case.req_to_token, case.req_pool_indices, case.seq_lens,
-            md["qo_indptr"], md["out_cache_loc"])
+            md["kv_indptr"], md["qo_indptr"], md["out_cache_loc"])
     assert OP.validate_step(*args)[0]
     bad_loc = md["out_cache_loc"].copy()
     bad_loc[0] += 1
-    assert not OP.validate_step(*args[:6], bad_loc)[0]
+    assert not OP.validate_step(*args[:7], bad_loc)[0]
     dup = md["out_cache_loc"].copy()
     dup[1] = dup[0]
-    assert not OP.validate_step(*args[:6], dup)[0]
+    assert not OP.validate_step(*args[:7], dup)[0]
     table = case.req_to_token.copy()
     table[case.req_pool_indices[0], 0] = case.size // ps
     assert not OP.validate_step(case.size, ps, table, *args[3:])[0]
     assert not OP.validate_step(case.size + 1, ps, *args[2:])[0]
+    kv = md["kv_indptr"].copy()
+    kv[1] += 1
+    assert not OP.validate_step(*args[:5], kv, *args[6:])[0]
+    qo = md["qo_indptr"].copy()
+    qo[0] = 1
+    assert not OP.validate_step(*args[:6], qo, args[7])[0]
 
 
 # ---------------------------------------------------------------------------
