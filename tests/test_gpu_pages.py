@@ -189,3 +189,64 @@ def test_paged_prefill_full_config_sampled():
                           case.seq_lens, qo, h["q"], case.sm_scale, rows)
     got = to_np(out)[[r for r, _ in rows], [hh for _, hh in rows]]
     assert_close(got, ref, "bf16", case.name)
+
+
+def test_paged_graph_decode_loop_crosses_pages():
+    """The graph-captured decode loop (rotary + K/V write, split attention,
+    merge, in-place metadata advance) over 16-token pages, with every request
+    crossing a page boundary during the loop; each replay is checked against
+    the oracle (the rotary write at the flat slots the paged oracle names,
+    then the paged attention)."""
+    import oracle
+    ps, steps = 16, 6
+    start = np.array([13, 30, 47], dtype=np.int32)   # first new token's position
+    H, Hk, d = 32, 8, 128
+    case = W.random_paged_case(970, list(start + steps + 1), ps, n_heads=H, n_kv_heads=Hk,
+                               head_dim=d, dtype="bf16")
+    say("paged graph loop", ps, start.tolist())
+    t = W.make_tensors(case, device="cuda", poison=False)
+    B_ = case.batch
+    rpi = case.req_pool_indices
+    step = api.DeviceStep(rpi, start + 1, case.req_to_token, max_len=int((start + steps).max()),
+                          page_size=ps)
+    freqs = W.rope_table(case.max_ctx_len, d, device="cuda")
+    q = torch.zeros((B_, H, d), dtype=torch.bfloat16, device="cuda")
+    k_new = torch.zeros((B_, Hk, d), dtype=torch.bfloat16, device="cuda")
+    v_new = torch.zeros_like(k_new)
+    q_rot = torch.empty_like(q)
+    out = torch.empty_like(q)
+    ns = 4
+    ws = api.decode_workspace(B_, H, d, ns)
+    kb_t, vb_t, tab = t["k_buffer"], t["v_buffer"], t["req_to_token"]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            api.rope_kv_store(kb_t, vb_t, tab, 0, step, q, k_new, v_new, freqs, q_out=q_rot)
+            api.decode_step(kb_t, vb_t, tab, 0, step, q_rot, None, None, case.sm_scale,
+                            num_splits=ns, workspace=ws, out=out, write_kv=False)
+            api.advance_decode(kb_t, vb_t, tab, step)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    kb = to_np(kb_t[0]).astype(np.float64)[None]
+    vb = to_np(vb_t[0]).astype(np.float64)[None]
+    f0 = freqs.cpu().numpy()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(971)
+    for k in range(steps):
+        for x in (q, k_new, v_new):
+            x.copy_(torch.randn(x.shape, generator=gen, device="cuda"))
+        q0, kn0, vn0 = to_np(q), to_np(k_new), to_np(v_new)
+        g.replay()
+        torch.cuda.synchronize()
+        pos = start + k
+        md = OP.build_step(rpi, pos + 1, case.req_to_token, ps)
+        q_ref, kb, vb = oracle.rope_kv_store(kb, vb, 0, md["out_cache_loc"], q0, kn0, vn0, pos,
+                                             f0, "bf16")
+        ref = OP.decode(kb, vb, 0, case.req_to_token, ps, rpi, pos + 1, q_ref, case.sm_scale)
+        assert_close(to_np(out), ref, "bf16", f"paged graph loop step {k}")
+        assert step.seq_lens.cpu().numpy().tolist() == (pos + 2).tolist()
