@@ -145,16 +145,17 @@ def test_paged_advance_matches_next_step_metadata():
 # ---------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("ps,q_lens,prefix,causal", [
-    (16, [1, 17, 64, 200], [0, 15, 33, 300], True),
-    (64, [130, 5, 1, 64], [64, 0, 700, 63], True),
-    (8, [40, 3], [9, 100], False),
-    (128, [300, 0, 129], [1, 5, 256], True),
-], ids=["p16", "p64", "p8_noncausal", "p128_empty_req"])
-def test_paged_prefill_matches_oracle(ps, q_lens, prefix, causal):
+@pytest.mark.parametrize("ps,q_lens,prefix,causal,d", [
+    (16, [1, 17, 64, 200], [0, 15, 33, 300], True, 128),
+    (64, [130, 5, 1, 64], [64, 0, 700, 63], True, 128),
+    (8, [40, 3], [9, 100], False, 128),
+    (128, [300, 0, 129], [1, 5, 256], True, 128),
+    (32, [70, 33, 1], [31, 0, 95], True, 64),
+], ids=["p16", "p64", "p8_noncausal", "p128_empty_req", "p32_d64"])
+def test_paged_prefill_matches_oracle(ps, q_lens, prefix, causal, d):
     lens = [p + q for p, q in zip(prefix, q_lens)]
     case = W.random_paged_case(400 + ps, lens, ps, q_lens=q_lens, n_heads=16, n_kv_heads=4,
-                               head_dim=128, dtype="bf16")
+                               head_dim=d, dtype="bf16")
     say("paged prefill", ps, q_lens, prefix, causal)
     t = W.make_tensors(case, device="cuda")
     h = host_layer(case, t)
