@@ -21,7 +21,7 @@ Sources (AstrAI project pages):
     decode kernel produces per-split partial outputs and (max, sum) pairs
     into a workspace, which a merge pass combines.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * GQA head map: query head h reads kv-head h // G with G = n_heads / n_kv_heads.
   * sm_scale is a parameter; the equation's value is 1/sqrt(head_dim).
   * Prefill is causal with the new tokens aligned to the end of the context:

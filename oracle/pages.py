@@ -18,7 +18,7 @@ Sources (AstrAI project pages):
   * "Inference" guide, section "KV Cache": the attention equation, evaluated
     here by ``oracle.attention.attend`` on the gathered rows.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * The flat pool k_buffer [n_layers, size, n_kv_heads, head_dim] with
     size = n_pages * page_size is the same memory as the page view
     [n_layers, n_pages, page_size, n_kv_heads, head_dim]; a flat slot index

@@ -17,7 +17,7 @@ Sources (AstrAI project pages):
   * "Inference" guide, section "KVCache System": the write is
     buffer[layer, out_cache_loc] = k.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * The table is an input; how it was filled (base frequency) is not part of
     this step.
   * The rotated values are rounded once to the pool dtype (bf16: round to
