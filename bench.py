@@ -351,6 +351,7 @@ def bench_prefill(reps=20, case=None):
     t = W.make_tensors(case, device="cuda", poison=False)
     step = api.DeviceStep(case.req_pool_indices, case.seq_lens, case.req_to_token, case.q_lens,
                           page_size=case.page_size)
+    step.set_prefill_blocks(case.n_heads, case.n_kv_heads)   # launch schedule of this step
     out = torch.empty_like(t["q"])
     lib = B.load()
     pool = B.make_pool(t["k_buffer"], t["v_buffer"], t["req_to_token"], case.page_size)

@@ -107,6 +107,11 @@ typedef struct {
   const int32_t *prefill_order;     /* [batch] or NULL: order in which prefill takes the
                                        requests (a permutation of 0..batch-1, e.g. the
                                        one pkv_build_step returns); affects speed only */
+  const int32_t *prefill_blocks;    /* [2 * n_prefill_blocks] or NULL: the prefill launch
+                                       schedule from pkv_prefill_blocks for this step and
+                                       head counts; prefill then launches exactly these
+                                       row blocks (prefill_order is not used) */
+  int64_t n_prefill_blocks;         /* host: entries (pairs) of prefill_blocks              */
 } pkv_step;
 
 /* Human-readable name of a status. Never NULL. */
@@ -157,6 +162,26 @@ pkv_status pkv_build_step(int32_t batch, const int32_t *req_pool_indices,
  * too small. */
 pkv_status pkv_build_positions(int32_t batch, const int32_t *seq_lens, const int32_t *q_lens,
                                int32_t *position_ids, int64_t capacity, int64_t *n_new);
+
+/* Host: the prefill launch schedule of a step (affects speed only).  The
+ * prefill kernel gives each workgroup one row block: up to
+ * PKV_PREFILL_BLOCK_ROWS query rows of one request, rows enumerating (new
+ * token t, query head g of a kv-head's group) as t * G + g, G = n_heads /
+ * n_kv_heads.  This lists every non-empty row block as a pair (request, row
+ * block index) in launch order: requests in the given order (order NULL:
+ * batch order; pkv_build_step's prefill_order puts the longest contexts
+ * first), and within a request the blocks of its last rows (the most keys
+ * under the causal mask) first.  Passed to pkv_paged_prefill through
+ * pkv_step.prefill_blocks, it launches no workgroup for rows that do not
+ * exist (without it the grid covers max_q_len rows of every request).
+ * All pointers are HOST memory; q_lens[b] new tokens of request b; blocks
+ * has room for `capacity` pairs; *n_blocks receives the count.
+ * PKV_ERR_SHAPE for bad head counts, a negative q_len or too small a
+ * capacity; PKV_ERR_BAD_METADATA when order is not a permutation. */
+#define PKV_PREFILL_BLOCK_ROWS 256
+pkv_status pkv_prefill_blocks(int32_t batch, const int32_t *q_lens, const int32_t *order,
+                              int32_t n_heads, int32_t n_kv_heads, int32_t *blocks,
+                              int64_t capacity, int64_t *n_blocks);
 
 /* Checked mode: validates HOST copies of one step's metadata against a pool
  * of `size` slots.  Accepts (PKV_OK) iff every request row is in
@@ -385,7 +410,11 @@ int32_t pkv_decode_step_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n
  * context); with causal == 0 it attends all kv_len_i keys.  QK^T and PV run
  * as bf16 matrix-core tiles with fp32 accumulation; the softmax weights are
  * rounded to bf16 before the PV product.  Uses step->max_q_len (host) to
- * size the launch.  Only PKV_BF16 pools are accepted (else PKV_ERR_DTYPE);
+ * size the launch, or, when step->prefill_blocks is set, launches exactly
+ * step->n_prefill_blocks row blocks per kv-head (the list must be
+ * pkv_prefill_blocks' for this step's q_lens and these head counts; like
+ * other device metadata it is not read on the host).  Only PKV_BF16 pools
+ * are accepted (else PKV_ERR_DTYPE);
  * sm_scale must be finite and > 0 (else PKV_ERR_SHAPE).
  * ---------------------------------------------------------------------- */
 pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,

@@ -40,11 +40,31 @@ class DeviceStep:
         # logical positions of the new tokens (rows of the rotary table)
         self.position_ids = to(B.pkv_build_positions(seq_lens, q_lens)) if self.n_new else \
             torch.zeros(0, dtype=torch.int32, device=device)
+        self.q_lens_host = None if q_lens is None else B._host_i32(q_lens, "q_lens")
+        self.prefill_blocks = None      # device schedule, set for given head counts
+        self.prefill_heads = None
+        self._make_c()
+
+    def _make_c(self):
         self.c = B.make_step(self.batch, self.req_pool_indices, self.seq_lens, self.kv_indptr,
                              None if self.decode else self.qo_indptr,
                              self.out_cache_loc if self.n_new else None, self.n_new,
                              self.max_len, self.max_q_len,
-                             None if self.decode else self.prefill_order)
+                             None if self.decode else self.prefill_order,
+                             self.prefill_blocks)
+
+    def set_prefill_blocks(self, n_heads: int, n_kv_heads: int) -> None:
+        """Build the prefill launch schedule (pkv_prefill_blocks) for these head
+        counts, copy it to the device once and attach it to the step."""
+        import torch
+        if self.decode or self.prefill_heads == (n_heads, n_kv_heads):
+            return
+        blocks = B.pkv_prefill_blocks(self.q_lens_host, self.host["prefill_order"], n_heads,
+                                      n_kv_heads)
+        self.prefill_blocks = (torch.from_numpy(np.ascontiguousarray(blocks.reshape(-1)))
+                               .to(self.req_pool_indices.device) if len(blocks) else None)
+        self.prefill_heads = (n_heads, n_kv_heads)
+        self._make_c()
 
 
 def decode_workspace(batch: int, n_heads: int, head_dim: int, num_splits: int, device="cuda"):
@@ -148,14 +168,18 @@ def rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceS
 
 
 def prefill_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q, k_new,
-                 v_new, sm_scale: float, causal: bool = True, out=None, write_kv: bool = True):
-    """K/V write of the step's new tokens, then ragged paged prefill."""
+                 v_new, sm_scale: float, causal: bool = True, out=None, write_kv: bool = True,
+                 schedule: bool = True):
+    """K/V write of the step's new tokens, then ragged paged prefill (with the
+    step's launch schedule of non-empty row blocks unless schedule=False)."""
     import torch
     if out is None:
         out = torch.empty_like(q)
     if write_kv:
         B.pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id, k_new, v_new,
                        step.out_cache_loc, page_size=step.page_size)
+    if schedule:
+        step.set_prefill_blocks(int(q.shape[1]), int(k_buffer.shape[2]))
     B.pkv_paged_prefill(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, sm_scale,
                         causal, out, page_size=step.page_size)
     return out

@@ -34,7 +34,7 @@ EXPORTED = (
     "pkv_kv_store", "pkv_decode_workspace_bytes", "pkv_decode_pick_splits",
     "pkv_paged_decode", "pkv_paged_decode_merge", "pkv_paged_prefill",
     "pkv_paged_decode_step", "pkv_decode_step_pick_splits", "pkv_paged_decode_store",
-    "pkv_build_positions", "pkv_rope_kv_store", "pkv_decode_advance",
+    "pkv_build_positions", "pkv_rope_kv_store", "pkv_decode_advance", "pkv_prefill_blocks",
 )
 
 
@@ -58,7 +58,8 @@ class pkv_step(C.Structure):
         ("batch", C.c_int32), ("req_pool_indices", C.c_void_p), ("seq_lens", C.c_void_p),
         ("kv_indptr", C.c_void_p), ("qo_indptr", C.c_void_p), ("out_cache_loc", C.c_void_p),
         ("n_new", C.c_int64), ("max_len", C.c_int32), ("max_q_len", C.c_int32),
-        ("prefill_order", C.c_void_p),
+        ("prefill_order", C.c_void_p), ("prefill_blocks", C.c_void_p),
+        ("n_prefill_blocks", C.c_int64),
     ]
 
 
@@ -106,6 +107,7 @@ def load() -> C.CDLL:
         "pkv_rope_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, i32, P, P, P, P, i64, P,
                                         i64, P]),
         "pkv_decode_advance": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, P, P, P, P]),
+        "pkv_prefill_blocks": (C.c_int, [i32, P, P, i32, i32, P, i64, C.POINTER(C.c_int64)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -196,7 +198,7 @@ def make_pool(k_buffer, v_buffer, req_to_token, page_size: int = 1) -> pkv_pool:
 
 def make_step(batch: int, req_pool_indices, seq_lens, kv_indptr=None, qo_indptr=None,
               out_cache_loc=None, n_new: Optional[int] = None, max_len: int = 0,
-              max_q_len: int = 1, prefill_order=None) -> pkv_step:
+              max_q_len: int = 1, prefill_order=None, prefill_blocks=None) -> pkv_step:
     """pkv_step view of device int32 tensors plus the host scalars."""
     import torch
     s = pkv_step()
@@ -210,6 +212,8 @@ def make_step(batch: int, req_pool_indices, seq_lens, kv_indptr=None, qo_indptr=
     s.max_len = int(max_len)
     s.max_q_len = int(max_q_len)
     s.prefill_order = _dev_ptr(prefill_order, "prefill_order", torch.int32)
+    s.prefill_blocks = _dev_ptr(prefill_blocks, "prefill_blocks", torch.int32)
+    s.n_prefill_blocks = 0 if prefill_blocks is None else int(prefill_blocks.numel()) // 2
     return s
 
 
@@ -244,6 +248,24 @@ def pkv_build_step(req_pool_indices, seq_lens, req_to_token, q_lens=None,
     return {"kv_indptr": kv, "qo_indptr": qo, "out_cache_loc": loc[:n_new.value].copy(),
             "n_new": n_new.value, "max_len": ml.value, "max_q_len": mq.value,
             "prefill_order": order[:B].copy()}
+
+
+def pkv_prefill_blocks(q_lens, order, n_heads: int, n_kv_heads: int) -> np.ndarray:
+    """Host: the prefill launch schedule, int32 [n_blocks, 2] of (request,
+    row block) pairs in launch order (order None: batch order)."""
+    ql = _host_i32(q_lens, "q_lens")
+    od = _host_i32(order, "order")
+    B = len(ql)
+    if od is not None and len(od) != B:
+        raise ValueError("order must hold one entry per request")
+    G = max(int(n_heads) // max(int(n_kv_heads), 1), 1)
+    cap = int(sum(-(-max(int(x), 0) * G // 256) for x in ql))
+    out = np.zeros((max(cap, 1), 2), dtype=np.int32)
+    n = C.c_int64(0)
+    st = load().pkv_prefill_blocks(B, _hp(ql), _hp(od), int(n_heads), int(n_kv_heads),
+                                   _hp(out), cap, C.byref(n))
+    _check(st, "pkv_prefill_blocks")
+    return out[:n.value].copy()
 
 
 def pkv_build_positions(seq_lens, q_lens=None) -> np.ndarray:

@@ -118,6 +118,8 @@ struct PrefillArgs {
   const int32_t *qo_indptr;
   const int32_t *kv_indptr;
   const int32_t *order;       // [batch] request processing order, or null
+  const int32_t *blocks;      // [2 * n_blocks] (request, row block) launch list, or null
+  int64_t n_blocks;
   const void *q;              // [n_new, n_heads, head_dim] bf16
   void *out;                  // [n_new, n_heads, head_dim] bf16
   int64_t pool_size;          // slots per layer
@@ -131,5 +133,6 @@ struct PrefillArgs {
   float scale_log2;
 };
 hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, hipStream_t stream);
+constexpr int kPrefillBlockRows = 256;  // query rows of one prefill workgroup
 
 }  // namespace pkv

@@ -164,6 +164,37 @@ pkv_status pkv_build_positions(int32_t batch, const int32_t *seq_lens, const int
   return PKV_OK;
 }
 
+static_assert(PKV_PREFILL_BLOCK_ROWS == pkv::kPrefillBlockRows, "prefill block rows");
+
+pkv_status pkv_prefill_blocks(int32_t batch, const int32_t *q_lens, const int32_t *order,
+                              int32_t n_heads, int32_t n_kv_heads, int32_t *blocks,
+                              int64_t capacity, int64_t *n_blocks) {
+  if (batch < 0 || n_heads <= 0 || n_kv_heads <= 0 || n_heads % n_kv_heads != 0 ||
+      capacity < 0)
+    return PKV_ERR_SHAPE;
+  if (!n_blocks) return PKV_ERR_NULL;
+  if (batch > 0 && !q_lens) return PKV_ERR_NULL;
+  const int64_t G = n_heads / n_kv_heads;
+  std::vector<char> hit((size_t)batch, 0);
+  int64_t n = 0;
+  for (int32_t j = 0; j < batch; ++j) {
+    const int32_t i = order ? order[j] : j;
+    if (i < 0 || i >= batch || hit[(size_t)i]) return PKV_ERR_BAD_METADATA;
+    hit[(size_t)i] = 1;
+    if (q_lens[i] < 0) return PKV_ERR_SHAPE;
+    const int64_t nblk = ((int64_t)q_lens[i] * G + pkv::kPrefillBlockRows - 1) /
+                         pkv::kPrefillBlockRows;
+    if (n + nblk > capacity) return PKV_ERR_SHAPE;
+    if (nblk > 0 && !blocks) return PKV_ERR_NULL;
+    for (int64_t x = 0; x < nblk; ++x, ++n) {  // last rows (most keys) first
+      blocks[2 * n] = i;
+      blocks[2 * n + 1] = (int32_t)(nblk - 1 - x);
+    }
+  }
+  *n_blocks = n;
+  return PKV_OK;
+}
+
 pkv_status pkv_validate_step(int64_t size, int64_t num_reqs, int64_t max_ctx_len,
                              int32_t page_size, const int32_t *req_to_token, int32_t batch,
                              const int32_t *req_pool_indices, const int32_t *seq_lens,
@@ -530,6 +561,10 @@ pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_s
   a.qo_indptr = step->qo_indptr;
   a.kv_indptr = step->kv_indptr;
   a.order = step->prefill_order;
+  a.blocks = step->prefill_blocks;
+  a.n_blocks = step->prefill_blocks ? step->n_prefill_blocks : 0;
+  if (a.blocks && (a.n_blocks <= 0 || a.n_blocks * pool->n_kv_heads > INT32_MAX))
+    return PKV_ERR_SHAPE;
   a.q = q;
   a.out = out;
   a.pool_size = pool->size;

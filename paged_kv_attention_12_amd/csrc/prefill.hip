@@ -48,6 +48,7 @@ constexpr int NT = 512;              // threads per workgroup (8 wavefronts)
 constexpr int BN = 64;               // keys per tile
 constexpr int WROWS = 32;            // query rows per wavefront
 constexpr int BM = NT / 64 * WROWS;  // query rows per workgroup
+static_assert(BM == kPrefillBlockRows, "row block size");
 constexpr int NBUF = 3;              // LDS tile buffers
 constexpr float kSlack = 8.f;        // log2 headroom before the running max is raised
 
@@ -88,6 +89,11 @@ struct Smem {
   uint16_t v[BN * VS];
 };
 
+// Query rows of request i: its new tokens times the group size.
+__device__ __forceinline__ int rows_of(const PrefillArgs &a, int i) {
+  return (a.qo_indptr[i + 1] - a.qo_indptr[i]) * a.group;
+}
+
 // OFF32: every row of the layer lies within 4 GiB of the layer base, so row
 // addresses are a uniform 64-bit base plus a 32-bit byte offset.  PAGED: the
 // table holds page ids of pages of 2^page_shift tokens (else slot ids).
@@ -109,18 +115,27 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   const int hk = lin % a.n_kv_heads;
   const int rest = lin / a.n_kv_heads;
   // Requests go in the caller's order (longest context first when it passes
-  // one), each request's row blocks together so they share L2.
-  const int ri = rest / a.row_blocks;
-  const int bx = rest - ri * a.row_blocks;
-  const int i = a.order ? a.order[ri] : ri;
+  // one), each request's row blocks together so they share L2, the block of
+  // the last rows (the most keys) first.  With a block list the launch holds
+  // exactly the non-empty blocks in that order; without one it covers
+  // row_blocks blocks of every request and the ones past its rows exit.
+  int i, rb;
+  if (a.blocks) {
+    i = a.blocks[2 * rest];
+    rb = a.blocks[2 * rest + 1];
+  } else {
+    const int ri = rest / a.row_blocks;
+    const int bx = rest - ri * a.row_blocks;
+    i = a.order ? a.order[ri] : ri;
+    const int nblk = (rows_of(a, i) + BM - 1) / BM;
+    if (bx >= nblk) return;
+    rb = nblk - 1 - bx;
+  }
   const int G = a.group;
   const int q0 = a.qo_indptr[i];
   const int q_len = a.qo_indptr[i + 1] - q0;
   const int kv_len = a.kv_indptr[i + 1] - a.kv_indptr[i];
   const int rows = q_len * G;
-  const int nblk = (rows + BM - 1) / BM;
-  if (bx >= nblk) return;
-  const int rb = nblk - 1 - bx;  // heaviest row block first
   const int prefix = kv_len - q_len;
 
   const int tid = threadIdx.x;
@@ -401,7 +416,7 @@ template <int D>
 hipError_t launch_d(const PrefillArgs &a, bool off32, hipStream_t stream) {
   const int64_t row_blocks = ((int64_t)a.max_q_len * a.group + BM - 1) / BM;
   if (row_blocks > INT32_MAX) return hipErrorInvalidValue;
-  const int64_t blocks = row_blocks * a.n_kv_heads * a.batch;
+  const int64_t blocks = (a.blocks ? a.n_blocks : row_blocks * a.batch) * a.n_kv_heads;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   PrefillArgs args = a;
   args.row_blocks = (int32_t)row_blocks;

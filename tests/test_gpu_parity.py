@@ -312,14 +312,33 @@ def test_prefill_q_len_one_matches_decode_oracle():
 
 
 def test_prefill_order_changes_nothing_but_schedule():
+    """The launch schedule (block list from pkv_prefill_blocks, in
+    prefill_order or in batch order) and the full grid (with or without
+    prefill_order) give bitwise the same output."""
     case = W.random_case(301, [700, 40, 2500, 9], [300, 40, 100, 9], n_heads=32, n_kv_heads=8,
                          head_dim=128, dtype="bf16")
     t = W.make_tensors(case, device="cuda")
-    step = api.DeviceStep(case.req_pool_indices, case.seq_lens, case.req_to_token, case.q_lens)
+    args = (case.req_pool_indices, case.seq_lens, case.req_to_token, case.q_lens)
+    step = api.DeviceStep(*args)
     assert step.host["prefill_order"].tolist() == [2, 0, 1, 3]
     o1 = api.prefill_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, step, t["q"],
                           t["k_new"], t["v_new"], case.sm_scale).clone()
-    step.c.prefill_order = None   # natural order
-    o2 = api.prefill_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, step, t["q"],
-                          t["k_new"], t["v_new"], case.sm_scale, write_kv=False)
-    assert torch.equal(o1, o2)
+    assert step.c.prefill_blocks and step.c.n_prefill_blocks == 5 + 1 + 2 + 1
+    outs = []
+    plain = api.DeviceStep(*args)
+    outs.append(api.prefill_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, plain, t["q"],
+                                 t["k_new"], t["v_new"], case.sm_scale, write_kv=False,
+                                 schedule=False).clone())
+    plain.c.prefill_order = None   # natural order, full grid
+    outs.append(api.prefill_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, plain, t["q"],
+                                 t["k_new"], t["v_new"], case.sm_scale, write_kv=False,
+                                 schedule=False).clone())
+    nat = api.DeviceStep(*args)    # block list in batch order
+    blocks = B.pkv_prefill_blocks(case.q_lens, None, 32, 8)
+    nat.prefill_blocks = torch.from_numpy(blocks.reshape(-1).copy()).cuda()
+    nat._make_c()
+    outs.append(api.prefill_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, nat, t["q"],
+                                 t["k_new"], t["v_new"], case.sm_scale, write_kv=False,
+                                 schedule=False).clone())
+    for o in outs:
+        assert torch.equal(o1, o)

@@ -468,3 +468,27 @@ def test_validate_step_random_corruptions_agree_with_oracle(lib, ps):
         assert lib_ok == ref_ok, (field, i, flat[i])
         n_bad += not lib_ok
     assert n_bad > 100
+
+
+def test_prefill_blocks_schedule(lib):
+    """pkv_prefill_blocks lists every non-empty row block of PKV_PREFILL_BLOCK_ROWS
+    query rows (token x group head), requests in the given order, the block of
+    the last rows first; errors for bad head counts, orders and q_lens."""
+    q_lens = [300, 0, 64, 65, 1]
+    order = [3, 0, 4, 2, 1]
+    got = B.pkv_prefill_blocks(q_lens, order, 32, 8)         # G = 4: 64 tokens per block
+    want = []
+    for i in order:
+        nblk = -(-q_lens[i] * 4 // 256)
+        want += [(i, nblk - 1 - x) for x in range(nblk)]
+    assert [tuple(x) for x in got.tolist()] == want
+    assert len(got) == 2 + 5 + 1 + 1
+    got1 = B.pkv_prefill_blocks(q_lens, None, 8, 8)          # G = 1: 256 tokens per block
+    assert [tuple(x) for x in got1.tolist()] == [(0, 1), (0, 0), (2, 0), (3, 0), (4, 0)]
+    for bad in (dict(n_heads=30, n_kv_heads=8), dict(n_heads=0, n_kv_heads=8)):
+        with pytest.raises(B.PkvError):
+            B.pkv_prefill_blocks(q_lens, order, **bad)
+    with pytest.raises(B.PkvError):
+        B.pkv_prefill_blocks(q_lens, [0, 0, 1, 2, 3], 32, 8)
+    with pytest.raises(B.PkvError):
+        B.pkv_prefill_blocks([5, -1], None, 32, 8)
