@@ -585,27 +585,50 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const StepArgs s
 
   const int newpos = NEW ? L - 1 : -1;
   const uint16_t *knew = nullptr, *vnew = nullptr;
+  // The new token's rows for the pool write: loaded here, stored after the
+  // attention, so the write adds no wait to this split's start-up chain.
+  bool writer = false;
+  uint4 new_piece = make_uint4(0u, 0u, 0u, 0u);
+  uint16_t *new_dst = nullptr;
   if constexpr (NEW) {
     const int64_t new_row = ((int64_t)b * a.n_kv_heads + hk) * D;  // element offset in k_new / v_new
     knew = reinterpret_cast<const uint16_t *>(sa.k_new) + new_row;
     vnew = reinterpret_cast<const uint16_t *>(sa.v_new) + new_row;
-    if (active && g0 == 0 && start <= newpos && newpos < end && lane < 2 * D / 8) {
+    writer = active && g0 == 0 && start <= newpos && newpos < end && lane < 2 * D / 8;
+    if (writer) {
       const int64_t loc = sa.out_cache_loc[b];
       const int64_t dst = (loc * a.n_kv_heads + hk) * D + 8 * (lane & 15);
-      if (lane < D / 8)
-        store16(reinterpret_cast<uint16_t *>(sa.k_layer_w) + dst, load16(knew + 8 * (lane & 15)));
-      else
-        store16(reinterpret_cast<uint16_t *>(sa.v_layer_w) + dst, load16(vnew + 8 * (lane & 15)));
+      new_piece = load16((lane < D / 8 ? knew : vnew) + 8 * (lane & 15));
+      new_dst = reinterpret_cast<uint16_t *>(lane < D / 8 ? sa.k_layer_w : sa.v_layer_w) + dst;
     }
   }
 
-  // An empty split (start >= end) runs no tile and writes the empty state
-  // o = 0, m = -inf, l = 0; there is no early exit, so that the loads of
-  // seq_lens[b] and req_pool_indices[b] above issue together.
+  // An empty split (start >= end, splits past a short request's length)
+  // writes the empty state o = 0, m = -inf, l = 0 and leaves before staging
+  // any slot id.  The asm operands make the length and the table row address
+  // ready before the branch, so the seq_lens[b], req_pool_indices[b] and
+  // table-argument loads all issue before it (an exit that needs only
+  // seq_lens[b] would let the compiler issue the others after it, lengthening
+  // the start-up chain of every non-empty split).
+  const int32_t *table_row = a.req_to_token + (int64_t)pool_row * a.table_stride;
+  asm volatile("" ::"s"(L), "s"(table_row), "s"(a.page_shift), "s"(a.max_ctx_len));
+  if (start >= end) {
+    if (active && col_ok) {
+      float4 *op = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) op[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (g == 0) {
+        a.ml_part[pr * 2 + 0] = kNegInf;
+        a.ml_part[pr * 2 + 1] = 0.f;
+      }
+    }
+    return;
+  }
   f32x4_t o[8];
   float m_run, l_tot;
   attend_mfma<1, NEW, kRing>(a, s_slot, b, pool_row, start, end, 0, active, hk, h0, col_ok, knew, vnew,
                              newpos, o, m_run, l_tot);
+  if (NEW && writer) store16(new_dst, new_piece);
   if (!active || !col_ok) return;
   // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
