@@ -626,8 +626,14 @@ __global__ void __launch_bounds__(256) decode_split_mfma_kernel(const StepArgs s
   }
   f32x4_t o[8];
   float m_run, l_tot;
-  attend_mfma<1, NEW, kRing>(a, s_slot, b, pool_row, start, end, 0, active, hk, h0, col_ok, knew, vnew,
-                             newpos, o, m_run, l_tot);
+  // Only the split holding the new token substitutes its rows in the fetch;
+  // every other split runs the plain loop.
+  if (NEW && start <= newpos && newpos < end)
+    attend_mfma<1, true, kRing>(a, s_slot, b, pool_row, start, end, 0, active, hk, h0, col_ok, knew,
+                                vnew, newpos, o, m_run, l_tot);
+  else
+    attend_mfma<1, false, kRing>(a, s_slot, b, pool_row, start, end, 0, active, hk, h0, col_ok,
+                                 nullptr, nullptr, -1, o, m_run, l_tot);
   if (NEW && writer) store16(new_dst, new_piece);
   if (!active || !col_ok) return;
   // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
