@@ -558,7 +558,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
 // position writes them to the pool slot out_cache_loc[b] (no wavefront of
 // the launch reads that pool row).
 template <bool NEW>
-__global__ void __launch_bounds__(256) decode_split_mfma_kernel(const StepArgs sa) {
+__global__ void __launch_bounds__(256, 2) decode_split_mfma_kernel(const StepArgs sa) {
   constexpr int D = kMfmaD;
   const DecodeArgs &a = sa.d;
   __shared__ int32_t s_slot[kSlotTile];
