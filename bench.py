@@ -250,6 +250,28 @@ def kernel_event_times(runner, launches, reps=3):
     return np.array(out)
 
 
+def kernel_launch_spread(runner, launches=100, warm=False):
+    """Per-launch durations of the split kernel: a HIP event pair on its stream
+    around each of `launches` eager launches; successive layers (cold: K/V
+    from HBM) or, with warm, the same layer every time (its 134 MB stay in the
+    last-level cache).  Returns (p10, p50, p90) in seconds."""
+    torch = runner.torch
+    st = runner.stream()
+    cur = torch.cuda.current_stream()
+    for k in range(3):
+        runner.decode(runner.layer_of(0 if warm else k), st)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for k, (a, b) in enumerate(ev):
+        a.record(cur)
+        runner.decode(runner.layer_of(0 if warm else k), st)
+        b.record(cur)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    return tuple(float(np.percentile(t, q)) for q in (10, 50, 90))
+
+
 # ---------------------------------------------------------------------------
 # graph-captured decode loop: one token of a 32-layer forward per replay
 # ---------------------------------------------------------------------------
@@ -556,6 +578,12 @@ def main():
                 "num_splits": head.num_splits}
     log(f"  step {sec_per_step * 1e6:.1f} us  {value:.0f} GB/s; split kernel {k_avg * 1e6:.1f} us "
         f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBPS:.1%})  graph_ok={graph_ok}")
+    cold = kernel_launch_spread(head)
+    warm = kernel_launch_spread(head, warm=True)
+    roofline["eager_launch_us_p10_p50_p90"] = [x * 1e6 for x in cold]
+    roofline["warm_launch_us_p10_p50_p90"] = [x * 1e6 for x in warm]
+    log(f"  split kernel per eager launch p10/p50/p90: {cold[0] * 1e6:.1f} / {cold[1] * 1e6:.1f} / "
+        f"{cold[2] * 1e6:.1f} us; warm (one layer, cached): {warm[1] * 1e6:.1f} us")
 
     extra = {}
     if not args.only_headline:
