@@ -93,7 +93,11 @@ typedef struct {
  * max_len may be any bound of seq_lens up to max_ctx_len, not only their
  * maximum: the kernels read seq_lens from device memory, so a captured graph
  * can replay steps whose lengths (and out_cache_loc, position_ids) the
- * caller advances in place between replays. */
+ * caller advances in place between replays.  A decode length that outgrows
+ * the bound is still attended whole (the last split takes the keys past
+ * num_splits times the split size, more slowly); a length past max_ctx_len
+ * cannot be addressed through the table, and every decode entry point then
+ * returns NaN for all heads of that request instead of reading anything. */
 typedef struct {
   int32_t batch;
   const int32_t *req_pool_indices;  /* [batch] row of req_to_token per request        */
@@ -256,7 +260,8 @@ int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_head
  * 0 .. seq_lens[b]-1 (the token written this step included; write it with
  * pkv_kv_store first) of layer layer_id.  Keys are split into num_splits
  * contiguous logical ranges of ceil(max_len / num_splits) tokens (rounded up
- * to a multiple of 16); each split's (m, l, o) partial goes to the workspace
+ * to a multiple of 16; the last range also takes any keys beyond
+ * num_splits such ranges); each split's (m, l, o) partial goes to the workspace
  * (layout above).  Call pkv_paged_decode_merge to form the output.
  * Errors: PKV_ERR_WORKSPACE_TOO_SMALL when ws_bytes <
  * pkv_decode_workspace_bytes(batch, n_heads, head_dim, num_splits).
@@ -286,9 +291,13 @@ pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_d
  *                      req_pool_indices[b] (pkv_pool's formula);
  *   kv_indptr[b] += b for b in [0, batch] (if not NULL).
  * All arrays are device int32 owned by the caller; the caller keeps every
- * length within max_ctx_len (a position past the row reads the row's last
- * entry instead).  The host max_len of the step must already bound the
- * lengths the next steps reach.  batch == 0 is a no-op.
+ * length within max_ctx_len.  Past it, out_cache_loc[b] is clamped to the
+ * slot of position max_ctx_len - 1 (a pkv_kv_store or pkv_rope_kv_store of
+ * that step overwrites that token; the one- and two-launch decode steps skip
+ * the write) and the decode entry points return NaN for the request (see
+ * pkv_step).  The host max_len of the step should bound the lengths the next
+ * steps reach (longer ones are attended correctly, but the last split takes
+ * the excess alone).  batch == 0 is a no-op.
  * Errors: PKV_ERR_NULL (missing seq_lens / req_pool_indices / out_cache_loc),
  * PKV_ERR_SHAPE (batch < 0).
  * ---------------------------------------------------------------------- */

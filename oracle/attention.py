@@ -318,25 +318,37 @@ def prefill_rows(k_buffer, v_buffer, layer_id, req_to_token, req_pool_indices,
     """Prefill output at selected (token, head) rows; token indexes the packed
     [n_new, H, d] query.  Request i owns tokens qo_indptr[i] .. qo_indptr[i+1]-1;
     its t-th new token sits at logical position p_i + t with
-    p_i = seq_len_i - q_len_i and, when causal, sees keys 0 .. p_i + t."""
+    p_i = seq_len_i - q_len_i and, when causal, sees keys 0 .. p_i + t.
+
+    Rows that share a request and a kv-head are evaluated together, so that
+    their keys are gathered once; each row still attends its own visible
+    keys.  Results come back in the order of ``rows``."""
     q = _f64(q)
     H = q.shape[1]
     Hk = k_buffer.shape[2]
     G = H // Hk
     qo = [int(x) for x in qo_indptr]
-    out = []
-    for tok, h in rows:
+    rows = [(int(tok), int(h)) for tok, h in rows]
+    out = np.zeros((len(rows), q.shape[2]), dtype=np.float64)
+    groups = {}
+    for n, (tok, h) in enumerate(rows):
         i = int(np.searchsorted(qo, tok, side="right")) - 1
+        groups.setdefault((i, h // G), []).append(n)
+    for (i, hk), members in groups.items():
         r = int(req_pool_indices[i])
         L = int(seq_lens[i])
         ql = qo[i + 1] - qo[i]
-        t = tok - qo[i]
-        nk = (L - ql + t + 1) if causal else L
-        slots = np.asarray(req_to_token[r, :nk], dtype=np.int64)
-        K = _gather(k_buffer, layer_id, slots, h // G)
-        V = _gather(v_buffer, layer_id, slots, h // G)
-        out.append(attend(q[tok, h], K, V, sm_scale)[0])
-    return np.stack(out) if out else np.zeros((0, q.shape[2]))
+        slots = np.asarray(req_to_token[r, :L], dtype=np.int64)
+        K = _gather(k_buffer, layer_id, slots, hk)
+        V = _gather(v_buffer, layer_id, slots, hk)
+        qs, nks = [], []
+        for n in members:
+            tok, h = rows[n]
+            t = tok - qo[i]
+            nks.append((L - ql + t + 1) if causal else L)
+            qs.append(q[tok, h])
+        out[members] = attend(np.stack(qs), K, V, sm_scale, nks)
+    return out
 
 
 def prefill(k_buffer, v_buffer, layer_id, req_to_token, req_pool_indices,

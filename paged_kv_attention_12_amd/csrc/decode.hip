@@ -61,6 +61,21 @@ __device__ __forceinline__ float slice_dot(const uint4 &q, const uint4 &k) {
 // Slot ids of one split are staged in LDS in rounds of this many tokens.
 constexpr int kSlotTile = 2048;
 
+// Keys of split s: [s * chunk, min(L, (s + 1) * chunk)), except that the last
+// split also takes every key past num_splits * chunk, so a request that has
+// grown past the host max_len the split size came from (a replayed graph
+// whose lengths advance on the device) is still attended whole, only more
+// slowly.  A length past max_ctx_len cannot be addressed through the table;
+// such a request attends nothing and its partials are NaN (split_overrun), so
+// the merged output is NaN instead of silently wrong.
+__device__ __forceinline__ bool split_overrun(const DecodeArgs &a, int L) {
+  return L > a.max_ctx_len;
+}
+__device__ __forceinline__ int split_end(const DecodeArgs &a, int s, int start, int L) {
+  if (split_overrun(a, L)) return start;
+  return s == a.num_splits - 1 ? L : min(L, start + a.chunk);
+}
+
 template <typename T, int D, int NG, int U>
 __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
   constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane per row
@@ -75,7 +90,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
   const int L = a.seq_lens[b];
   const int pool_row = a.req_pool_indices[b];
   const int start = s * a.chunk;
-  const int end = min(L, start + a.chunk);
+  const int end = split_end(a, s, start, L);
 
   const int lane = threadIdx.x & 63;
   const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -91,14 +106,16 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
   const int64_t p0 = ((int64_t)b * a.n_heads + h0) * S + s;  // partial row of head h0
 
   if (start >= end) {  // empty split (uniform over the workgroup): (-inf, 0), o = 0
+    const bool bad = split_overrun(a, L);
+    const float ov = bad ? NAN : 0.f;
     if (active && row == 0) {
       for (int g = 0; g < ng; ++g) {
         float4 *o = reinterpret_cast<float4 *>(a.o_part + (p0 + (int64_t)g * S) * D + part * EPL);
 #pragma unroll
-        for (int e = 0; e < EPL; e += 4) o[e / 4] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int e = 0; e < EPL; e += 4) o[e / 4] = make_float4(ov, ov, ov, ov);
         if (part == 0) {
-          a.ml_part[(p0 + (int64_t)g * S) * 2 + 0] = kNegInf;
-          a.ml_part[(p0 + (int64_t)g * S) * 2 + 1] = 0.f;
+          a.ml_part[(p0 + (int64_t)g * S) * 2 + 0] = bad ? NAN : kNegInf;
+          a.ml_part[(p0 + (int64_t)g * S) * 2 + 1] = bad ? 1.f : 0.f;
         }
       }
     }
@@ -522,8 +539,10 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
   // Ring of P register tile sets: P - 1 tiles are in flight while one is used.
   static_assert(P >= 2, "pipeline depth");
   uint4 kr[P][2][4], vr[P][8];
-  for (int r0 = start; r0 < end; r0 += kSlotTile) {
-    const int r1 = min(end, r0 + kSlotTile);
+  // Rounds of run_cap keys: a split of up to one chunk takes one round (or
+  // rounds of kSlotTile), the last split's tail past num_splits * chunk more.
+  for (int r0 = start; r0 < end; r0 += run_cap) {
+    const int r1 = min(end, r0 + run_cap);
     if (r0 != start) {
       __syncthreads();
       load_run(r0);
@@ -568,7 +587,7 @@ __global__ void __launch_bounds__(256, 2) decode_split_mfma_kernel(const StepArg
   const int L = a.seq_lens[b];
   const int pool_row = a.req_pool_indices[b];
   const int start = s * a.chunk;
-  const int end = min(L, start + a.chunk);
+  const int end = split_end(a, s, start, L);
 
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
@@ -613,13 +632,15 @@ __global__ void __launch_bounds__(256, 2) decode_split_mfma_kernel(const StepArg
   const int32_t *table_row = a.req_to_token + (int64_t)pool_row * a.table_stride;
   asm volatile("" ::"s"(L), "s"(table_row), "s"(a.page_shift), "s"(a.max_ctx_len));
   if (start >= end) {
+    const bool bad = split_overrun(a, L);
+    const float ov = bad ? NAN : 0.f;
     if (active && col_ok) {
       float4 *op = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) op[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int i = 0; i < 8; ++i) op[i] = make_float4(ov, ov, ov, ov);
       if (g == 0) {
-        a.ml_part[pr * 2 + 0] = kNegInf;
-        a.ml_part[pr * 2 + 1] = 0.f;
+        a.ml_part[pr * 2 + 0] = bad ? NAN : kNegInf;
+        a.ml_part[pr * 2 + 1] = bad ? 1.f : 0.f;
       }
     }
     return;
@@ -674,7 +695,6 @@ __device__ __forceinline__ float load_agent(const float *p) {
 // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15): wait for this wave's vector
 // memory operations only.
 constexpr int kWaitVmem0 = 0x0F70;
-
 __global__ void __launch_bounds__(256, 2) decode_step_kernel(const StepArgs sa) {
   constexpr int D = kMfmaD;
   const DecodeArgs &a = sa.d;
@@ -698,7 +718,7 @@ __global__ void __launch_bounds__(256, 2) decode_step_kernel(const StepArgs sa) 
   const int L = a.seq_lens[b];
   const int pool_row = a.req_pool_indices[b];
   const int start = s * a.chunk;
-  const int end = min(L, start + a.chunk);
+  const int end = split_end(a, s, start, L);
   const int hk = task / a.n_chunks;
   const int chunk_i = task - hk * a.n_chunks;
   const int g0 = chunk_i * a.heads_per_chunk;
@@ -771,32 +791,39 @@ __global__ void __launch_bounds__(256, 2) decode_step_kernel(const StepArgs sa) 
       }
       // Device-scope stores: the partial is read by whichever workgroup (on
       // any XCD) merges, so it must not wait in this XCD's L2.
+      // A request past max_ctx_len attended nothing: its partial is NaN.
+      const bool bad = split_overrun(a, L);
       const int64_t pr = ((int64_t)b * a.n_heads + h0 + hc) * S + s;
       float *op = a.o_part + pr * D + d0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) store_agent(op + e, acc[e] * inv);
+      for (int e = 0; e < 8; ++e) store_agent(op + e, bad ? NAN : acc[e] * inv);
       if ((tid & 15) == 0) {
-        store_agent(a.ml_part + pr * 2 + 0, lsum > 0.f ? M : kNegInf);
-        store_agent(a.ml_part + pr * 2 + 1, lsum);
+        store_agent(a.ml_part + pr * 2 + 0, bad ? NAN : (lsum > 0.f ? M : kNegInf));
+        store_agent(a.ml_part + pr * 2 + 1, bad ? 1.f : lsum);
       }
     }
   }
 
-  // Ticket: the last split of (b, task) to finish merges.  Release: every
-  // thread's device-scope partial stores have completed (vmcnt 0) before the
-  // barrier, and the barrier before the ticket.  The partials are the only
-  // data another workgroup reads, so no L2 write-back is needed.
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  // Ticket: the last split of (b, task) to finish merges.  The hand-off is
+  // a release / acquire pair at agent scope: the workgroup barrier orders
+  // every thread's partial stores before thread 0's ticket, the ticket is an
+  // agent-scope release read-modify-write, and the workgroup that draws the
+  // last ticket issues an agent-scope acquire fence before it reads any
+  // partial.  By the HIP memory model the merging workgroup therefore sees
+  // every partial of the (b, task) row, whichever XCD wrote it.  Each wave
+  // also waits for its own partial stores to complete before the barrier
+  // (s_waitcnt vmcnt(0)), so the ticket is never drawn while a store of the
+  // workgroup is still in flight.
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   __syncthreads();
   if (tid == 0) {
     const int t = __hip_atomic_fetch_add(&sa.sync[(int64_t)b * sa.tasks + task], 1,
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                         __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     s_last = t == S - 1;
   }
   __syncthreads();
   if (!s_last) return;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   // Merge: wave w takes heads w, w + 4, ...; lane l dims 2l, 2l + 1.  Up to
   // 32 splits per memory round trip.

@@ -200,20 +200,18 @@ def test_decode_batched_prefix_full():
     assert_close(to_np(out), hv.decode_all(case), "bf16", "batched")
 
 
-@pytest.mark.parametrize("num_splits", [64, 128])
-def test_decode_long_context_sampled(num_splits):
+def test_decode_long_context_every_head():
+    """B=8 x 131072, 64 query heads over 8 kv-heads, keys x4: every head of
+    every request against the oracle, at 64 and at 128 splits."""
     case = W.long_context_decode()
-    say("long context decode", num_splits)
+    say("long context decode: host copy")
     t = W.make_tensors(case, device="cuda")
-    reqs = [0, 7]
-    hv = HostView(case, t, requests=reqs)
-    out = to_np(gpu_decode(case, t, num_splits=num_splits))
-    rng = np.random.default_rng(num_splits)
-    pairs = [(b, int(h)) for b in reqs for h in rng.choice(64, 8, replace=False)]
-    ref = hv.decode_pairs(case, pairs)
-    got = np.stack([out[b, h] for b, h in pairs])
-    assert_close(got, ref, "bf16", "long")
-    assert np.isfinite(out).all()
+    hv = HostView(case, t)
+    ref = hv.decode_all(case)
+    for num_splits in (64, 128):
+        say("long context decode", num_splits)
+        out = to_np(gpu_decode(case, t, num_splits=num_splits))
+        assert_close(out, ref, "bf16", f"long, {num_splits} splits")
 
 
 def test_decode_many_empty_splits():
@@ -276,7 +274,11 @@ def test_prefill_sharp_and_rising_scores(d, causal):
                  f"prefill sharp d{d}")
 
 
-def test_prefill_full_config_sampled():
+def test_prefill_full_config_block_edges_every_head():
+    """16-request ragged causal prefill: every head of the first and the last
+    token of every 256-row block of every request (the rows a launch block
+    starts and ends with, the diagonal tiles of the causal mask), plus random
+    rows, against the oracle."""
     case = W.ragged_prefill()
     say("ragged prefill full")
     t = W.make_tensors(case, device="cuda")
@@ -284,13 +286,17 @@ def test_prefill_full_config_sampled():
     out = to_np(gpu_prefill(case, t))
     assert np.isfinite(out).all()
     qo = hv.md["qo_indptr"]
+    G = case.n_heads // case.n_kv_heads
+    tok_per_block = 256 // G
     rng = np.random.default_rng(4)
-    rows = []
+    toks = set()
     for i in range(case.batch):
-        toks = {int(qo[i]), int(qo[i + 1]) - 1}
-        toks |= set(int(x) for x in rng.integers(qo[i], qo[i + 1], size=6))
-        for tok in sorted(toks):
-            rows.append((tok, int(rng.integers(0, case.n_heads))))
+        q0, q1 = int(qo[i]), int(qo[i + 1])
+        for b0 in range(q0, q1, tok_per_block):
+            toks |= {b0, min(b0 + tok_per_block, q1) - 1}
+        toks |= set(int(x) for x in rng.integers(q0, q1, size=6))
+    rows = [(tok, h) for tok in sorted(toks) for h in range(case.n_heads)]
+    say("prefill oracle rows", len(rows))
     ref = hv.prefill_rows(case, rows)
     got = np.stack([out[tok, h] for tok, h in rows])
     assert_close(got, ref, "bf16", "prefill full")

@@ -8,6 +8,10 @@ in fp64): every (b, h) pair of a G = 4 and a G = 6 batch, on one-token pages
 and on 16-token pages, must give decode()'s row.  Mistakes planted in copies
 of the samplers (head map h % Hk, the slot row cut one short, the pair's
 request taken as its table row) must fail the same comparison.
+``oracle.prefill_rows`` (which groups its rows by request and kv-head) is
+held to the full ``prefill()`` the same way, causal and not, with rows asked
+for in a shuffled order; copies with a wrong head map or a causal limit one
+key short fail.
 """
 
 import numpy as np
@@ -167,3 +171,60 @@ def test_planted_sampler_mistake_is_caught(name, head_of, cut, row_of):
     for H, Hk in SHAPES:
         assert not _flat_sampler_matches(_flat_mutant(head_of, cut, row_of), 104, H, Hk), name
         assert not _paged_sampler_matches(_paged_mutant(head_of, cut, row_of), 105, H, Hk), name
+
+
+# ---------------------------------------------------------------------------
+# prefill_rows: every (token, head) row of a G = 4 and a G = 6 ragged batch,
+# asked for in a shuffled order, equals the full prefill's row.
+# ---------------------------------------------------------------------------
+def _prefill_case(seed, H, Hk):
+    q_lens, prefix = [5, 1, 0, 9], [3, 12, 4, 0]
+    lens = [a + b for a, b in zip(q_lens, prefix)]
+    case = W.random_case(seed, lens, q_lens, n_heads=H, n_kv_heads=Hk, head_dim=16)
+    t = np_tensors(case)
+    kb, vb, md = store_new(case, t)
+    return case, t, kb, vb, md
+
+
+def _prefill_rows_match(fn, seed, H, Hk, causal) -> bool:
+    case, t, kb, vb, md = _prefill_case(seed, H, Hk)
+    full = oracle.prefill(kb, vb, 0, case.req_to_token, case.req_pool_indices, case.seq_lens,
+                          md["qo_indptr"], t["q"], case.sm_scale, causal=causal)
+    rows = [(tok, h) for tok in range(md["n_new"]) for h in range(H)]
+    np.random.default_rng(seed).shuffle(rows)
+    got = fn(kb, vb, 0, case.req_to_token, case.req_pool_indices, case.seq_lens,
+             md["qo_indptr"], t["q"], case.sm_scale, rows, causal=causal)
+    want = np.stack([full[tok, h] for tok, h in rows])
+    return got.shape == want.shape and bool(np.allclose(got, want, rtol=0, atol=1e-14))
+
+
+@pytest.mark.parametrize("H,Hk", SHAPES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_rows_equals_prefill_every_row(H, Hk, causal):
+    assert _prefill_rows_match(oracle.prefill_rows, 106, H, Hk, causal)
+
+
+def _prefill_rows_mutant(head_of, causal_shift):
+    def fn(k_buffer, v_buffer, layer_id, req_to_token, req_pool_indices, seq_lens, qo_indptr, q,
+           sm_scale, rows, causal=True):
+        q = np.asarray(q, np.float64)
+        H, Hk = q.shape[1], k_buffer.shape[2]
+        G = H // Hk
+        qo = [int(x) for x in qo_indptr]
+        out = []
+        for tok, h in rows:
+            i = int(np.searchsorted(qo, tok, side="right")) - 1
+            L, ql, t = int(seq_lens[i]), qo[i + 1] - qo[i], tok - qo[i]
+            nk = (L - ql + t + 1 - causal_shift) if causal else L
+            slots = np.asarray(req_to_token[int(req_pool_indices[i]), :max(nk, 1)], np.int64)
+            hk = head_of(h, G, Hk)
+            out.append(OA.attend(q[tok, h], k_buffer[layer_id, slots, hk, :],
+                                 v_buffer[layer_id, slots, hk, :], sm_scale)[0])
+        return np.stack(out)
+    return fn
+
+
+def test_prefill_rows_planted_mistakes_are_caught():
+    assert _prefill_rows_match(_prefill_rows_mutant(_RIGHT_HEAD, 0), 107, 12, 2, True)
+    assert not _prefill_rows_match(_prefill_rows_mutant(_MOD_HEAD, 0), 107, 12, 2, True)
+    assert not _prefill_rows_match(_prefill_rows_mutant(_RIGHT_HEAD, 1), 107, 12, 2, True)
