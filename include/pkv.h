@@ -21,8 +21,10 @@
  *   - "device" pointers are HIP device memory of the current device; "host"
  *     pointers are ordinary CPU memory.  The caller owns every buffer.
  *   - The library never allocates or frees device memory, never synchronises
- *     the device, and keeps no state between calls except cached device
- *     properties; calls are re-entrant and thread-safe.
+ *     the device, and keeps no state between calls except the per-device
+ *     address of its one static scratch array (pkv_paged_decode_store_noalloc);
+ *     calls are re-entrant and thread-safe, except that calls of that one
+ *     entry point which overlap on one device share its scratch and race.
  *   - Kernels are enqueued on the caller's stream and return before they run.
  *   - Host-checkable arguments are validated and reported as a pkv_status;
  *     nothing is launched when a check fails.  Device-resident metadata is
@@ -52,7 +54,8 @@ typedef enum {
   PKV_ERR_WORKSPACE_TOO_SMALL = 4,  /* workspace below the required size     */
   PKV_ERR_BAD_METADATA = 5,         /* pkv_validate_step / pkv_build_step    */
   PKV_ERR_HIP = 6,                  /* a HIP runtime call or launch failed   */
-  PKV_ERR_UNSUPPORTED = 7           /* valid but not implemented (head_dim)  */
+  PKV_ERR_UNSUPPORTED = 7,          /* valid but not implemented (head_dim)  */
+  PKV_ERR_SCRATCH_LIMIT = 8         /* needs more than the static scratch    */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -398,6 +401,29 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
                                   const void *q, const void *k_new, const void *v_new,
                                   int32_t n_heads, float sm_scale, int32_t num_splits,
                                   void *workspace, size_t ws_bytes, void *out, void *stream);
+
+/* ----------------------------------------------------------------------
+ * The decode step of pkv_paged_decode_store without a caller workspace, for
+ * callers that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, result
+ * and kernels as pkv_paged_decode_store, minus workspace / ws_bytes: the
+ * split partials go to a static device array of PKV_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on every device it runs on until the process
+ * ends (its address is looked up on the first call on each device).  Nothing
+ * is allocated or freed.  Every call on a device shares that device's array:
+ * calls that overlap on one device (other streams, other threads) race and
+ * must be serialised by the caller; calls in order on one stream do not
+ * (each call rewrites every partial it reads).
+ * Errors: as pkv_paged_decode_store, plus PKV_ERR_SCRATCH_LIMIT when
+ * pkv_decode_workspace_bytes(batch, n_heads, head_dim, num_splits) exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES (nothing is launched), and PKV_ERR_HIP when the
+ * array's address cannot be obtained.
+ * ---------------------------------------------------------------------- */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+pkv_status pkv_paged_decode_store_noalloc(const pkv_pool *pool, int32_t layer_id,
+                                          const pkv_step *step, const void *q, const void *k_new,
+                                          const void *v_new, int32_t n_heads, float sm_scale,
+                                          int32_t num_splits, void *out, void *stream);
 
 /* Host-only split count for pkv_paged_decode_step: the single-wave choice of
  * pkv_decode_pick_splits divided by four (each split of the fused step is

@@ -25,6 +25,7 @@ PKV_ERR_WORKSPACE_TOO_SMALL = 4
 PKV_ERR_BAD_METADATA = 5
 PKV_ERR_HIP = 6
 PKV_ERR_UNSUPPORTED = 7
+PKV_ERR_SCRATCH_LIMIT = 8
 
 PKV_F32 = 0
 PKV_BF16 = 1
@@ -35,6 +36,7 @@ EXPORTED = (
     "pkv_paged_decode", "pkv_paged_decode_merge", "pkv_paged_prefill",
     "pkv_paged_decode_step", "pkv_decode_step_pick_splits", "pkv_paged_decode_store",
     "pkv_build_positions", "pkv_rope_kv_store", "pkv_decode_advance", "pkv_prefill_blocks",
+    "pkv_paged_decode_store_noalloc",
 )
 
 
@@ -103,6 +105,9 @@ def load() -> C.CDLL:
         "pkv_decode_step_pick_splits": (i32, [i32, i32, i32, i32, i64, i32]),
         "pkv_paged_decode_store": (C.c_int, [C.POINTER(pkv_pool), i32, C.POINTER(pkv_step), P, P,
                                              P, i32, f32, i32, P, sz, P, P]),
+        "pkv_paged_decode_store_noalloc": (C.c_int, [C.POINTER(pkv_pool), i32,
+                                                     C.POINTER(pkv_step), P, P, P, i32, f32, i32,
+                                                     P, P]),
         "pkv_build_positions": (C.c_int, [i32, P, P, P, i64, C.POINTER(C.c_int64)]),
         "pkv_rope_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, i32, P, P, P, P, i64, P,
                                         i64, P]),
@@ -401,6 +406,26 @@ def pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id: int, step
         _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _dev_ptr(out, "out"), _stream())
     _check(st, "pkv_paged_decode_store")
+
+
+def pkv_paged_decode_store_noalloc(k_buffer, v_buffer, req_to_token, layer_id: int,
+                                   step: pkv_step, q, k_new, v_new, sm_scale: float,
+                                   num_splits: int, out, page_size: int = 1) -> None:
+    """pkv_paged_decode_store with the split partials in the library's static
+    per-device scratch array instead of a caller workspace."""
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
+    if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
+            or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q / out must be [batch, n_heads, head_dim] in the pool dtype")
+    if tuple(k_new.shape) != (step.batch,) + tuple(k_buffer.shape[2:]) \
+            or k_new.shape != v_new.shape or k_new.dtype != k_buffer.dtype \
+            or v_new.dtype != k_buffer.dtype:
+        raise ValueError("k_new / v_new must be [batch, n_kv_heads, head_dim] in the pool dtype")
+    st = load().pkv_paged_decode_store_noalloc(
+        C.byref(pool), int(layer_id), C.byref(step), _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"),
+        _dev_ptr(v_new, "v_new"), int(q.shape[1]), float(sm_scale), int(num_splits),
+        _dev_ptr(out, "out"), _stream())
+    _check(st, "pkv_paged_decode_store_noalloc")
 
 
 def pkv_rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, q, q_out, k_new, v_new,

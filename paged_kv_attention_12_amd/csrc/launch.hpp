@@ -7,6 +7,10 @@
 
 namespace pkv {
 
+// Records e as the calling thread's last HIP error (pkv_last_hip_error) and
+// returns PKV_ERR_HIP (as an int: pkv_status lives in the C header).
+int note_hip_error(hipError_t e);
+
 struct KvStoreArgs {
   void *k_layer;              // k_buffer + layer_id * size * row_elems (bytes as char*)
   void *v_layer;

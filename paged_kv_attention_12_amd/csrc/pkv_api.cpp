@@ -78,6 +78,11 @@ int32_t decode_chunk(int32_t max_len, int32_t num_splits) {
 
 }  // namespace
 
+int pkv::note_hip_error(hipError_t e) {
+  g_last_hip_error = (int32_t)e;
+  return PKV_ERR_HIP;
+}
+
 extern "C" {
 
 const char *pkv_status_string(pkv_status s) {
@@ -90,6 +95,7 @@ const char *pkv_status_string(pkv_status s) {
     case PKV_ERR_BAD_METADATA: return "inconsistent step metadata";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_SCRATCH_LIMIT: return "workspace needed exceeds the static scratch buffer";
   }
   return "unknown status";
 }

@@ -40,8 +40,9 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         assert lib.pkv_status_string(s)
+    assert B.status_string(B.PKV_ERR_SCRATCH_LIMIT).startswith("workspace needed exceeds")
     assert B.status_string(B.PKV_ERR_WORKSPACE_TOO_SMALL) == "workspace too small"
 
 
