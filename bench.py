@@ -179,6 +179,36 @@ class StoredDecodeRunner(DecodeRunner):
         assert r == 0, r
 
 
+class SharedDecodeRunner(DecodeRunner):
+    """The same workload stepped through pkv_paged_decode_shared: each prefix
+    group's shared keys read once (groups from pkv_decode_prefix_groups on the
+    host table), the requests' own keys with the new-token K/V write, the
+    merge.  decode() is the whole shared step (three launches)."""
+
+    def __init__(self, case, fill_all_layers=True, min_prefix=256):
+        from paged_kv_attention_12_amd import api, binding as B
+        super().__init__(case, fill_all_layers)
+        c = self.case
+        self.groups = api.PrefixGroups(self.step, c.req_pool_indices, c.seq_lens,
+                                       c.req_to_token, min_prefix=min_prefix)
+        self.num_splits, self.prefix_splits = self.groups.pick_splits(self.step, c.n_kv_heads,
+                                                                      c.n_heads)
+        self.ws = api.decode_workspace(c.batch, c.n_heads, c.head_dim,
+                                       self.num_splits + self.prefix_splits)
+        self.ws_bytes = self.ws.numel() * 4
+        self.groups_ref = C.byref(self.groups.c)
+
+    def run_step(self, layer):
+        r = self.lib.pkv_paged_decode_shared(
+            self.pool_ref, layer, self.step_ref, self.groups_ref, self.ptr["q"], self.ptr["k_new"],
+            self.ptr["v_new"], self.case.n_heads, self.scale, self.num_splits, self.prefix_splits,
+            self.ws.data_ptr(), self.ws_bytes, self.out.data_ptr(), self.stream())
+        assert r == 0, r
+
+    def decode(self, layer, st):
+        self.run_step(layer)
+
+
 def graph_steps(runner, n, start=0):
     """Capture n consecutive steps (layer rotation from step `start`) in one graph."""
     torch = runner.torch
@@ -450,28 +480,43 @@ def bench_prefill(reps=20, case=None):
 # ---------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the headline workload)
 # ---------------------------------------------------------------------------
-def cpu_baseline(runner, budget_s=15.0):
-    import oracle
+def _threads():
+    """(os.cpu_count(), BLAS threads numpy uses)."""
+    n = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = n
+    return int(n), int(blas)
+
+
+def _host_layer(t, case, slots):
+    """Host float32 copies of the attended layer's rows at `slots` (sorted),
+    and the request table renumbered onto them."""
     import torch
-    case = runner.case
-    layer = case.layer_id
-    slots = case.referenced_slots()
     idx = torch.from_numpy(slots).cuda()
-    k = runner.t["k_buffer"][layer].index_select(0, idx).float().cpu().numpy()[None]
-    v = runner.t["v_buffer"][layer].index_select(0, idx).float().cpu().numpy()[None]
+    layer = case.layer_id
+    k = t["k_buffer"][layer].index_select(0, idx).float().cpu().numpy()[None]
+    v = t["v_buffer"][layer].index_select(0, idx).float().cpu().numpy()[None]
     table = np.zeros_like(case.req_to_token)
     for b in range(case.batch):
         r = int(case.req_pool_indices[b])
         L = int(case.seq_lens[b])
         table[r, :L] = np.searchsorted(slots, case.req_to_token[r, :L])
+    return k, v, table
+
+
+def cpu_baseline(runner, budget_s=10.0):
+    """The oracle on the headline decode step: whole steps (write + attention
+    of every head), repeated for about budget_s."""
+    import oracle
+    case = runner.case
+    k, v, table = _host_layer(runner.t, case, case.referenced_slots())
     q = runner.t["q"].float().cpu().numpy()
     kn = runner.t["k_new"].float().cpu().numpy()
     vn = runner.t["v_new"].float().cpu().numpy()
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    n_cpu, blas = _threads()
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -483,11 +528,94 @@ def cpu_baseline(runner, budget_s=15.0):
         if dt >= budget_s or n >= 200:
             break
     per = dt / n
-    return {"value": runner.step_bytes() / per / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": runner.step_bytes() / per / 1e9, "unit": "GB/s", "cores": blas,
+            "kind": "oracle", "os_cpu_count": n_cpu, "blas_threads": blas,
             "sample": f"{n} full decode steps of {case.name} (kv_store + attention of all "
                       f"{case.n_heads} heads over {int(case.seq_lens[0])} keys), numpy fp64, "
                       f"{per * 1e3:.1f} ms/step"}
+
+
+def cpu_baseline_long_context(runner, budget_s=8.0):
+    """The oracle on the long-context decode: (request, query head) rows of
+    one kv-head group at a time (all 131072 keys each), repeated over
+    requests for about budget_s; reported on the K/V bytes those rows read."""
+    import oracle
+    case = runner.case
+    G = case.n_heads // case.n_kv_heads
+    n_cpu, blas = _threads()
+    rows = 0
+    groups = 0
+    t_work = 0.0
+    for b in range(case.batch):
+        slots = np.unique(case.req_to_token[int(case.req_pool_indices[b]),
+                                            :int(case.seq_lens[b])].astype(np.int64))
+        k, v, table = _host_layer(runner.t, case, slots)
+        q = runner.t["q"][b:b + 1].float().cpu().numpy()
+        for hk in range(case.n_kv_heads):
+            pairs = [(0, hk * G + g) for g in range(G)]
+            t0 = time.perf_counter()
+            oracle.decode_pairs(k, v, 0, table, case.req_pool_indices[b:b + 1],
+                                case.seq_lens[b:b + 1], q, case.sm_scale, pairs)
+            t_work += time.perf_counter() - t0
+            rows += G
+            groups += 1
+            if t_work >= budget_s:
+                break
+        del k, v
+        if t_work >= budget_s:
+            break
+    L = int(case.seq_lens[0])
+    sampled = groups * L * (2 * case.head_dim * 2 + 4)   # K+V row of one kv-head + slot id
+    return {"value": sampled / t_work / 1e9, "unit": "GB/s", "cores": blas, "kind": "oracle",
+            "os_cpu_count": n_cpu, "blas_threads": blas,
+            "sample": f"{rows} (request, head) rows = {groups} kv-head groups x {L} keys of "
+                      f"{case.name}, numpy fp64, {t_work:.1f} s; rate on the K/V bytes they read",
+            "full_call_s_extrapolated": t_work / groups * case.batch * case.n_kv_heads}
+
+
+def cpu_baseline_prefill(budget_s=8.0, seed=7):
+    """The oracle on the ragged prefill: all query heads of random new tokens
+    of every request, in rounds, for about budget_s; reported in TFLOP/s on
+    the unmasked (query, key) pairs of the rows evaluated."""
+    import oracle
+    import workloads as W
+    case = W.ragged_prefill()
+    t = W.make_tensors(case, device="cuda", poison=False)
+    k, v, table = _host_layer(t, case, case.referenced_slots())
+    md = oracle.build_step(case.req_pool_indices, case.seq_lens, table, case.q_lens)
+    k, v = oracle.kv_store(k, v, 0, md["out_cache_loc"], t["k_new"].float().cpu().numpy(),
+                           t["v_new"].float().cpu().numpy())
+    q = t["q"].float().cpu().numpy()
+    del t
+    qo = md["qo_indptr"]
+    rng = np.random.default_rng(seed)
+    n_cpu, blas = _threads()
+    d, H = case.head_dim, case.n_heads
+    flops = 0
+    n_rows = 0
+    t_work = 0.0
+    while t_work < budget_s:
+        rows = []
+        for i in range(case.batch):
+            q0, q1 = int(qo[i]), int(qo[i + 1])
+            if q1 == q0:
+                continue
+            tok = int(rng.integers(q0, q1))
+            p = int(case.seq_lens[i]) - (q1 - q0)
+            flops += 4 * d * H * (p + tok - q0 + 1)
+            rows += [(tok, h) for h in range(H)]
+        t0 = time.perf_counter()
+        oracle.prefill_rows(k, v, 0, table, case.req_pool_indices, case.seq_lens, qo, q,
+                            case.sm_scale, rows)
+        t_work += time.perf_counter() - t0
+        n_rows += len(rows)
+    rate = flops / t_work
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": blas, "kind": "oracle",
+            "os_cpu_count": n_cpu, "blas_threads": blas,
+            "sample": f"{n_rows} (token, head) rows of ragged_causal_prefill_16req (one random "
+                      f"new token per request per round, all {H} heads), numpy fp64, "
+                      f"{t_work:.1f} s; FLOPs of their unmasked (query, key) pairs",
+            "full_call_s_extrapolated": prefill_flops(case) / rate}
 
 
 # ---------------------------------------------------------------------------
@@ -586,6 +714,7 @@ def main():
         f"{cold[2] * 1e6:.1f} us; warm (one layer, cached): {warm[1] * 1e6:.1f} us")
 
     extra = {}
+    cpu_long = None
     if not args.only_headline:
         sweep = {}
         for L in W.LLAMA_SWEEP:
@@ -629,6 +758,22 @@ def main():
             "num_splits": rb.num_splits, "graph_ok": ok}
         del rb
         torch.cuda.empty_cache()
+        rs = SharedDecodeRunner(W.batched_prefix_decode())
+        sps, oks = timed_graph(rs, 20, 3)
+        kts = kernel_event_times(rs, 8, reps=2)
+        extra["batched_prefix_decode"]["shared_prefix"] = {
+            "step_us": sps * 1e6, "step_event_us": float(kts.mean()) * 1e6,
+            "gbps_unique": rs.unique_kernel_bytes() / sps / 1e9,
+            "frac_of_hbm_peak_unique": rs.unique_kernel_bytes() / sps / 1e9 / HBM_PEAK_GBPS,
+            "gbps_logical": rs.kernel_bytes() / sps / 1e9,
+            "num_splits": rs.num_splits, "prefix_splits": rs.prefix_splits,
+            "n_groups": rs.groups.n_groups, "graph_ok": oks,
+            "step": "pkv_paged_decode_shared: shared keys once per group + own keys with the "
+                    "K/V write + merge"}
+        log(f"  shared-prefix step {sps * 1e6:.1f} us ({rs.groups.n_groups} groups), plain step "
+            f"{extra['batched_prefix_decode']['step_us']:.1f} us")
+        del rs
+        torch.cuda.empty_cache()
 
         log("long-context decode")
         rl = DecodeRunner(W.long_context_decode())
@@ -639,6 +784,9 @@ def main():
             "gbps": rl.kernel_bytes() / float(ktl.mean()) / 1e9,
             "frac_of_hbm_peak": rl.kernel_bytes() / float(ktl.mean()) / 1e9 / HBM_PEAK_GBPS,
             "num_splits": rl.num_splits, "graph_ok": ok}
+        if not args.no_cpu_baseline:
+            log("cpu oracle baseline: long-context decode sample")
+            cpu_long = cpu_baseline_long_context(rl)
         del rl
         torch.cuda.empty_cache()
 
@@ -677,8 +825,12 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu oracle baseline")
+        log("cpu oracle baseline: headline decode")
         cpu = cpu_baseline(head)
+        if not args.only_headline:
+            cpu["long_context_decode"] = cpu_long
+            log("cpu oracle baseline: prefill sample")
+            cpu["prefill"] = cpu_baseline_prefill()
 
     rec = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

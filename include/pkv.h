@@ -425,6 +425,75 @@ pkv_status pkv_paged_decode_store_noalloc(const pkv_pool *pool, int32_t layer_id
                                           const void *v_new, int32_t n_heads, float sm_scale,
                                           int32_t num_splits, void *out, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Decode with shared prefixes ("Inference" guide, section "KVCache System":
+ * the allocator and prefix cache let requests share the slots of a common
+ * prompt prefix; commit history of tests/inference/test_cache.py: request
+ * mappings are rebuilt for cached prefix pages).  When several requests of a
+ * step read the same slots for their first P positions, the decode step can
+ * read those keys once per group instead of once per request: one launch
+ * attends every group's shared keys with all members' query heads together,
+ * the split kernel attends each request's keys from kv_start[b] = P on, and
+ * the merge combines both.  The result is the same function as
+ * pkv_paged_decode_store (the same per-head softmax over all seq_lens[b]
+ * keys); only the order of the fp32 sums differs.
+ *
+ * A group record is PKV_PREFIX_GROUP_INTS int32: [P, m, b_0 .. b_{m-1}, 0 ..]
+ * with 2 <= m <= PKV_PREFIX_GROUP_MAX members (batch indices) whose table
+ * rows agree on every entry of positions 0 .. P-1 and whose seq_lens exceed
+ * P (each request's newest position stays its own).
+ * ---------------------------------------------------------------------- */
+#define PKV_PREFIX_GROUP_MAX 16
+#define PKV_PREFIX_GROUP_INTS (2 + PKV_PREFIX_GROUP_MAX)
+
+typedef struct {
+  const int32_t *groups;    /* device [n_groups * PKV_PREFIX_GROUP_INTS] group records      */
+  const int32_t *kv_start;  /* device [batch]: P of the request's group, 0 for none          */
+  int32_t n_groups;
+  int32_t max_prefix;       /* host: largest P                                              */
+  int32_t max_members;      /* host: largest member count                                   */
+  int32_t max_suffix;       /* host: bound of seq_lens[b] - kv_start[b] over the batch      */
+} pkv_prefix_groups;
+
+/* Host: the prefix groups of a decode step, from HOST copies of its metadata
+ * and table (page_size as in pkv_pool).  Requests whose first table entries
+ * agree are grouped: each group takes a lead (the longest such request,
+ * the earliest on ties) and the requests sharing the most leading positions with it
+ * (at most PKV_PREFIX_GROUP_MAX members), with P the smallest shared range
+ * among them, chosen to maximise (members - 1) * P; groups with P <
+ * min_prefix are not formed, and the other requests are grouped again among
+ * themselves.  A request's shared range never includes its last position.
+ * Writes *n_groups records to groups (capacity groups_cap records),
+ * kv_start[batch] (P or 0), and the host bounds *max_prefix, *max_members,
+ * *max_suffix (max of seq_lens[b] - kv_start[b]).  Affects speed only: any
+ * valid grouping, or none, gives the same result.
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (bad page size, too small a capacity),
+ * PKV_ERR_BAD_METADATA (request row or length out of range). */
+pkv_status pkv_decode_prefix_groups(int32_t batch, const int32_t *req_pool_indices,
+                                    const int32_t *seq_lens, const int32_t *req_to_token,
+                                    int64_t num_reqs, int64_t max_ctx_len, int32_t page_size,
+                                    int32_t min_prefix, int32_t *groups, int64_t groups_cap,
+                                    int64_t *n_groups, int32_t *kv_start, int32_t *max_prefix,
+                                    int32_t *max_members, int32_t *max_suffix);
+
+/* The decode step of pkv_paged_decode_store (new-token K/V write, attention,
+ * merge; same arguments and contract) with the shared prefixes of `groups`
+ * (device arrays from pkv_decode_prefix_groups for this step's metadata and
+ * tables) read once per group.  num_splits splits cover each request's own
+ * keys [kv_start[b], seq_lens[b]) (split size from groups->max_suffix; the
+ * last split takes any excess), prefix_splits splits each group's shared
+ * keys.  workspace: pkv_decode_workspace_bytes(batch, n_heads, head_dim,
+ * num_splits + prefix_splits) bytes.  Three launches (shared keys, own keys
+ * with the K/V write, merge) for bf16 pools with head_dim 128; with groups
+ * NULL or n_groups 0, or other pools, this is pkv_paged_decode_store.
+ * Errors: as pkv_paged_decode_store, plus PKV_ERR_SHAPE for prefix_splits
+ * outside [1, 65535] or inconsistent host bounds in groups. */
+pkv_status pkv_paged_decode_shared(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,
+                                   const pkv_prefix_groups *groups, const void *q,
+                                   const void *k_new, const void *v_new, int32_t n_heads,
+                                   float sm_scale, int32_t num_splits, int32_t prefix_splits,
+                                   void *workspace, size_t ws_bytes, void *out, void *stream);
+
 /* Host-only split count for pkv_paged_decode_step: the single-wave choice of
  * pkv_decode_pick_splits divided by four (each split of the fused step is
  * taken by four wavefronts), clamped to [1, max_splits]. */

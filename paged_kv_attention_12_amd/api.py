@@ -143,6 +143,55 @@ def stored_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: De
     return out
 
 
+class PrefixGroups:
+    """The prefix groups of one decode step (pkv_decode_prefix_groups on the
+    host copies of its metadata and table), copied to the device once."""
+
+    def __init__(self, step: "DeviceStep", req_pool_indices, seq_lens, req_to_token_host,
+                 min_prefix: int = 256, device="cuda"):
+        import torch
+        h = B.pkv_decode_prefix_groups(req_pool_indices, seq_lens, req_to_token_host,
+                                       step.page_size, min_prefix)
+        self.host = h
+        self.n_groups = h["n_groups"]
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+        self.groups = to(h["groups"].reshape(-1)) if self.n_groups else \
+            torch.zeros(B.PKV_PREFIX_GROUP_INTS, dtype=torch.int32, device=device)
+        self.kv_start = to(h["kv_start"])
+        self.c = B.make_prefix_groups(self.groups, self.kv_start, self.n_groups, h["max_prefix"],
+                                      h["max_members"], h["max_suffix"])
+        self.suffix_total = int(np.sum(np.asarray(seq_lens, dtype=np.int64) - h["kv_start"]))
+
+    def pick_splits(self, step: "DeviceStep", n_kv_heads: int, n_heads: int):
+        """(num_splits, prefix_splits): the split heuristic on the requests'
+        own keys, and prefix splits of about 256 shared keys."""
+        ns = B.pkv_decode_pick_splits(step.batch, n_kv_heads, n_heads,
+                                      max(self.host["max_suffix"], 1), self.suffix_total)
+        ps = max(1, -(-self.host["max_prefix"] // 256)) if self.n_groups else 1
+        return ns, ps
+
+
+def shared_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep,
+                       groups: PrefixGroups, q, k_new, v_new, sm_scale: float,
+                       num_splits: Optional[int] = None, prefix_splits: Optional[int] = None,
+                       workspace=None, out=None):
+    """The decode step with each prefix group's shared keys read once
+    (pkv_paged_decode_shared).  Returns out."""
+    import torch
+    H, d = int(q.shape[1]), int(q.shape[2])
+    ns, ps = groups.pick_splits(step, int(k_buffer.shape[2]), H)
+    num_splits = ns if num_splits is None else num_splits
+    prefix_splits = ps if prefix_splits is None else prefix_splits
+    if workspace is None:
+        workspace = decode_workspace(step.batch, H, d, num_splits + prefix_splits, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    B.pkv_paged_decode_shared(k_buffer, v_buffer, req_to_token, layer_id, step.c, groups.c, q,
+                              k_new, v_new, sm_scale, num_splits, prefix_splits, workspace, out,
+                              page_size=step.page_size)
+    return out
+
+
 def advance_decode(k_buffer, v_buffer, req_to_token, step: DeviceStep) -> None:
     """Move a decode step's device metadata to the next token in place (one
     launch; graph-capturable).  step.max_len must already bound the lengths

@@ -36,8 +36,11 @@ EXPORTED = (
     "pkv_paged_decode", "pkv_paged_decode_merge", "pkv_paged_prefill",
     "pkv_paged_decode_step", "pkv_decode_step_pick_splits", "pkv_paged_decode_store",
     "pkv_build_positions", "pkv_rope_kv_store", "pkv_decode_advance", "pkv_prefill_blocks",
-    "pkv_paged_decode_store_noalloc",
+    "pkv_paged_decode_store_noalloc", "pkv_decode_prefix_groups", "pkv_paged_decode_shared",
 )
+
+PKV_PREFIX_GROUP_MAX = 16
+PKV_PREFIX_GROUP_INTS = 2 + PKV_PREFIX_GROUP_MAX
 
 
 class PkvError(RuntimeError):
@@ -62,6 +65,13 @@ class pkv_step(C.Structure):
         ("n_new", C.c_int64), ("max_len", C.c_int32), ("max_q_len", C.c_int32),
         ("prefill_order", C.c_void_p), ("prefill_blocks", C.c_void_p),
         ("n_prefill_blocks", C.c_int64),
+    ]
+
+
+class pkv_prefix_groups(C.Structure):
+    _fields_ = [
+        ("groups", C.c_void_p), ("kv_start", C.c_void_p), ("n_groups", C.c_int32),
+        ("max_prefix", C.c_int32), ("max_members", C.c_int32), ("max_suffix", C.c_int32),
     ]
 
 
@@ -108,6 +118,11 @@ def load() -> C.CDLL:
         "pkv_paged_decode_store_noalloc": (C.c_int, [C.POINTER(pkv_pool), i32,
                                                      C.POINTER(pkv_step), P, P, P, i32, f32, i32,
                                                      P, P]),
+        "pkv_decode_prefix_groups": (C.c_int, [i32, P, P, P, i64, i64, i32, i32, P, i64,
+                                               C.POINTER(C.c_int64), P, P, P, P]),
+        "pkv_paged_decode_shared": (C.c_int, [C.POINTER(pkv_pool), i32, C.POINTER(pkv_step),
+                                              C.POINTER(pkv_prefix_groups), P, P, P, i32, f32,
+                                              i32, i32, P, sz, P, P]),
         "pkv_build_positions": (C.c_int, [i32, P, P, P, i64, C.POINTER(C.c_int64)]),
         "pkv_rope_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, i32, P, P, P, P, i64, P,
                                         i64, P]),
@@ -426,6 +441,63 @@ def pkv_paged_decode_store_noalloc(k_buffer, v_buffer, req_to_token, layer_id: i
         _dev_ptr(v_new, "v_new"), int(q.shape[1]), float(sm_scale), int(num_splits),
         _dev_ptr(out, "out"), _stream())
     _check(st, "pkv_paged_decode_store_noalloc")
+
+
+def pkv_decode_prefix_groups(req_pool_indices, seq_lens, req_to_token, page_size: int = 1,
+                             min_prefix: int = 256) -> dict:
+    """Host prefix groups of a decode step: dict with groups (int32
+    [n_groups, PKV_PREFIX_GROUP_INTS]), kv_start (int32 [batch]) and the ints
+    n_groups, max_prefix, max_members, max_suffix."""
+    rpi = _host_i32(req_pool_indices, "req_pool_indices")
+    sl = _host_i32(seq_lens, "seq_lens")
+    table = _host_i32(req_to_token, "req_to_token")
+    if table.ndim != 2 or len(rpi) != len(sl):
+        raise ValueError("req_to_token must be 2-D and the batch arrays equal in length")
+    B = len(sl)
+    cap = max(B // 2, 1)
+    groups = np.zeros((cap, PKV_PREFIX_GROUP_INTS), dtype=np.int32)
+    kv_start = np.zeros(max(B, 1), dtype=np.int32)
+    ng = C.c_int64(0)
+    mp, mm, ms = (np.zeros(1, dtype=np.int32) for _ in range(3))
+    st = load().pkv_decode_prefix_groups(
+        B, _hp(rpi), _hp(sl), _hp(table), table.shape[0], table.shape[1] * max(page_size, 1),
+        int(page_size), int(min_prefix), _hp(groups), cap, C.byref(ng), _hp(kv_start), _hp(mp),
+        _hp(mm), _hp(ms))
+    _check(st, "pkv_decode_prefix_groups")
+    return {"groups": groups[:ng.value].copy(), "kv_start": kv_start[:B].copy(),
+            "n_groups": int(ng.value), "max_prefix": int(mp[0]), "max_members": int(mm[0]),
+            "max_suffix": int(ms[0])}
+
+
+def make_prefix_groups(groups_dev, kv_start_dev, n_groups: int, max_prefix: int,
+                       max_members: int, max_suffix: int) -> pkv_prefix_groups:
+    import torch
+    g = pkv_prefix_groups()
+    g.groups = _dev_ptr(groups_dev, "groups", torch.int32)
+    g.kv_start = _dev_ptr(kv_start_dev, "kv_start", torch.int32)
+    g.n_groups, g.max_prefix = int(n_groups), int(max_prefix)
+    g.max_members, g.max_suffix = int(max_members), int(max_suffix)
+    return g
+
+
+def pkv_paged_decode_shared(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step,
+                            groups: Optional[pkv_prefix_groups], q, k_new, v_new,
+                            sm_scale: float, num_splits: int, prefix_splits: int, workspace,
+                            out, page_size: int = 1) -> None:
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
+    if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
+            or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q / out must be [batch, n_heads, head_dim] in the pool dtype")
+    if tuple(k_new.shape) != (step.batch,) + tuple(k_buffer.shape[2:]) \
+            or k_new.shape != v_new.shape or k_new.dtype != k_buffer.dtype \
+            or v_new.dtype != k_buffer.dtype:
+        raise ValueError("k_new / v_new must be [batch, n_kv_heads, head_dim] in the pool dtype")
+    st = load().pkv_paged_decode_shared(
+        C.byref(pool), int(layer_id), C.byref(step), C.byref(groups) if groups is not None else None,
+        _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"), int(q.shape[1]),
+        float(sm_scale), int(num_splits), int(prefix_splits), _dev_ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _dev_ptr(out, "out"), _stream())
+    _check(st, "pkv_paged_decode_shared")
 
 
 def pkv_rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, q, q_out, k_new, v_new,

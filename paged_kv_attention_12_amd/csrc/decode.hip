@@ -272,11 +272,32 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const MergeArgs a) {
   __shared__ float s_den[SG];
   const int r = blockIdx.x;
   const int t = threadIdx.x;
-  const int S = a.num_splits;
+  // Splits of this row (rows are a.stride splits apart).  Without seq_lens:
+  // all num_splits (empty ones hold weight-0 partials).  With seq_lens, only
+  // the splits that hold keys were written: own split s covers keys from
+  // kv_start + s * chunk (the last one any excess), prefix split s keys from
+  // s * prefix_chunk below P = kv_start; those partials sit after the own
+  // num_splits in the row, so both are read as one run with a gap skipped.
+  int S = a.num_splits, n_own = a.num_splits;
+  if (a.seq_lens) {
+    const int b = r / a.n_heads;
+    const int base = a.kv_start ? a.kv_start[b] : 0;
+    const int len = a.seq_lens[b] - base;
+    n_own = len <= 0 ? 0 : min(a.num_splits, (len + a.chunk - 1) / a.chunk);
+    if (a.seq_lens[b] > a.max_ctx_len) n_own = a.num_splits;  // NaN partials, all written
+    const int n_pfx = base > 0 ? min(a.prefix_splits, (base + a.prefix_chunk - 1) / a.prefix_chunk)
+                               : 0;
+    S = n_own + n_pfx;
+  } else if (a.kv_start && a.kv_start[r / a.n_heads] > 0) {
+    S = a.num_splits + a.prefix_splits;
+    n_own = S;
+  }
+  // slot of the k-th split read: own splits first, then the prefix ones
+  const int gap = a.num_splits - n_own;
   const int sg = t / TPR;
   const int c = t - sg * TPR;
-  const float *ml = a.ml_part + (int64_t)r * S * 2;
-  const float *op = a.o_part + (int64_t)r * S * D + c * 4;
+  const float *ml = a.ml_part + (int64_t)r * a.stride * 2;
+  const float *op = a.o_part + (int64_t)r * a.stride * D + c * 4;
 
   float den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -289,7 +310,8 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const MergeArgs a) {
     float mv[KB], lv[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      const int s = min(s0 + SG * k, S - 1);
+      const int sk = min(s0 + SG * k, S - 1);
+      const int s = sk < n_own ? sk : sk + gap;
       ov[k] = *reinterpret_cast<const float4 *>(op + (int64_t)s * D);
       mv[k] = ml[2 * s];
       lv[k] = (s0 + SG * k < S) ? ml[2 * s + 1] : 0.f;
@@ -388,15 +410,18 @@ constexpr int kKT = 32;      // keys per iteration of a wavefront
 // within each staged run the wavefront takes the 32-key tiles first,
 // first + TS, first + 2 TS, ...  With NEW the key at position newpos is read
 // from the rows knew / vnew (this kv-head's K and V of the token written in
-// the same step) instead of the pool.  pool_row is req_pool_indices[b], read by
-// the caller together with seq_lens[b] so that the two loads share one memory
-// round trip.  On return o[e][i] holds the
-// unnormalised O[head c][32g + 8i + e] against the base-2 running max m_run,
-// and l_tot the running sum (both per head, equal in the four lane groups).
+// the same step) instead of the pool.  pool_row is the table row the keys are
+// read through (req_pool_indices of the request, read by the caller together
+// with seq_lens so that the two loads share one memory round trip).  qcol is
+// the query row of this lane's column (a query head of one request), or null
+// for an unused column.  Runs of staged slot ids hold a.chunk keys (at most
+// kSlotTile).  On return o[e][i] holds the
+// unnormalised O[column c][32g + 8i + e] against the base-2 running max m_run,
+// and l_tot the running sum (both per column, equal in the four lane groups).
 template <int TS, bool NEW, int P>
-__device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot, int b, int pool_row,
+__device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot, int pool_row,
                                             int start, int end, int first, bool active, int hk,
-                                            int h0, bool col_ok, const uint16_t *knew,
+                                            const uint16_t *qcol, const uint16_t *knew,
                                             const uint16_t *vnew, int newpos, f32x4_t (&o)[8],
                                             float &m_run, float &l_tot) {
   constexpr int D = kMfmaD;
@@ -428,15 +453,11 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
   };
   load_run(start);  // first on the dependent chain to the K/V rows
 
-  // Q^T operand: head c, dims 8g + 32k .. +8 for step k.
+  // Q^T operand: column c, dims 8g + 32k .. +8 for step k.
   uint4 qf[4];
-  {
-    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) +
-                           ((int64_t)b * a.n_heads + h0 + c) * D + 8 * g;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      qf[k] = (active && col_ok) ? load16(qrow + 32 * k) : make_uint4(0u, 0u, 0u, 0u);
-  }
+  for (int k = 0; k < 4; ++k)
+    qf[k] = (active && qcol) ? load16(qcol + 8 * g + 32 * k) : make_uint4(0u, 0u, 0u, 0u);
 
   const int64_t row_elems = (int64_t)a.n_kv_heads * D;
   const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k_layer) + (int64_t)hk * D + 8 * g;
@@ -577,29 +598,28 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
 // position writes them to the pool slot out_cache_loc[b] (no wavefront of
 // the launch reads that pool row).
 template <bool NEW>
-__global__ void __launch_bounds__(256, 2) decode_split_mfma_kernel(const StepArgs sa) {
+__device__ __forceinline__ void split_mfma_body(const StepArgs &sa, int32_t *s_slot, int b, int s,
+                                                int wx) {
   constexpr int D = kMfmaD;
   const DecodeArgs &a = sa.d;
-  __shared__ int32_t s_slot[kSlotTile];
 
-  const int b = blockIdx.z;
-  const int s = blockIdx.y;
   const int L = a.seq_lens[b];
   const int pool_row = a.req_pool_indices[b];
-  const int start = s * a.chunk;
+  // With a shared prefix the request's own splits start at kv_start[b].
+  const int start = (a.kv_start ? a.kv_start[b] : 0) + s * a.chunk;
   const int end = split_end(a, s, start, L);
 
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int g = lane >> 4;
-  const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int task = wx * 4 + (threadIdx.x >> 6);
   const bool active = task < a.n_kv_heads * a.n_chunks;
   const int hk = active ? task / a.n_chunks : 0;
   const int g0 = active ? (task - hk * a.n_chunks) * a.heads_per_chunk : 0;
   const int ng = active ? min(a.heads_per_chunk, a.group - g0) : 0;
   const int h0 = hk * a.group + g0;
   const bool col_ok = c < ng;
-  const int S = a.num_splits;
+  const int S = a.split_stride;
   const int64_t pr = ((int64_t)b * a.n_heads + h0 + c) * S + s;  // partial row of head h0 + c
 
   const int newpos = NEW ? L - 1 : -1;
@@ -630,9 +650,11 @@ __global__ void __launch_bounds__(256, 2) decode_split_mfma_kernel(const StepArg
   // seq_lens[b] would let the compiler issue the others after it, lengthening
   // the start-up chain of every non-empty split).
   const int32_t *table_row = a.req_to_token + (int64_t)pool_row * a.table_stride;
-  asm volatile("" ::"s"(L), "s"(table_row), "s"(a.page_shift), "s"(a.max_ctx_len));
+  asm volatile("" ::"s"(L), "s"(table_row), "s"(a.page_shift), "s"(a.max_ctx_len), "s"(start));
   if (start >= end) {
     const bool bad = split_overrun(a, L);
+    // With skip_empty the merge reads only the splits that hold keys.
+    if (a.skip_empty && !bad) return;
     const float ov = bad ? NAN : 0.f;
     if (active && col_ok) {
       float4 *op = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
@@ -649,12 +671,15 @@ __global__ void __launch_bounds__(256, 2) decode_split_mfma_kernel(const StepArg
   float m_run, l_tot;
   // Only the split holding the new token substitutes its rows in the fetch;
   // every other split runs the plain loop.
+  const uint16_t *qcol =
+      col_ok ? reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)b * a.n_heads + h0 + c) * D
+             : nullptr;
   if (NEW && start <= newpos && newpos < end)
-    attend_mfma<1, true, kRing>(a, s_slot, b, pool_row, start, end, 0, active, hk, h0, col_ok, knew,
-                                vnew, newpos, o, m_run, l_tot);
+    attend_mfma<1, true, kRing>(a, s_slot, pool_row, start, end, 0, active, hk, qcol, knew, vnew,
+                                newpos, o, m_run, l_tot);
   else
-    attend_mfma<1, false, kRing>(a, s_slot, b, pool_row, start, end, 0, active, hk, h0, col_ok,
-                                 nullptr, nullptr, -1, o, m_run, l_tot);
+    attend_mfma<1, false, kRing>(a, s_slot, pool_row, start, end, 0, active, hk, qcol, nullptr,
+                                 nullptr, -1, o, m_run, l_tot);
   if (NEW && writer) store16(new_dst, new_piece);
   if (!active || !col_ok) return;
   // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
@@ -668,6 +693,110 @@ __global__ void __launch_bounds__(256, 2) decode_split_mfma_kernel(const StepArg
   if (g == 0) {
     a.ml_part[pr * 2 + 0] = m_run;
     a.ml_part[pr * 2 + 1] = l_tot;
+  }
+}
+
+template <bool NEW>
+__global__ void __launch_bounds__(256, 2) decode_split_mfma_kernel(const StepArgs sa) {
+  __shared__ int32_t s_slot[kSlotTile];
+  split_mfma_body<NEW>(sa, s_slot, blockIdx.z, blockIdx.y, blockIdx.x);
+}
+
+// ---------------------------------------------------------------------------
+// Shared-prefix decode (bf16, head_dim 128).  The members of a prefix group
+// read the same slots for their first P positions, so those keys are
+// gathered once per group: a wavefront owns (group, prefix split, kv-head,
+// 16 columns), where the columns enumerate (member, query head of the
+// kv-head's group) as member * G + head, and it runs the same matrix-core
+// routine as the split kernel with those columns as the query rows.  Each
+// column's (m, l, o) partial goes to its member's partial row, after the
+// member's own num_splits splits (which the split kernel runs over keys
+// [kv_start[b], seq_lens[b]) = [P, seq_lens[b])).  The merge weighs both.
+__device__ __forceinline__ void prefix_mfma_body(const PrefixArgs &pa, int32_t *s_slot, int grp,
+                                                 int s, int wx) {
+  constexpr int D = kMfmaD;
+  const DecodeArgs &a = pa.d;
+
+  const int32_t *rec = pa.groups + (int64_t)grp * pa.group_ints;
+  const int P = rec[0];
+  const int m = rec[1];
+  const int pool_row = a.req_pool_indices[rec[2]];  // any member's row: same slots below P
+  const int start = s * a.chunk;
+  const int end = s == pa.prefix_splits - 1 ? P : min(P, start + a.chunk);
+
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  const int G = a.group;
+  const int n_cc = (m * G + 15) >> 4;  // 16-column chunks of this group per kv-head
+  const int task = wx * 4 + (threadIdx.x >> 6);
+  const bool active = task < a.n_kv_heads * n_cc;
+  const int hk = active ? task / n_cc : 0;
+  const int idx = (active ? task - hk * n_cc : 0) * 16 + c;
+  const int member = idx / G;
+  const bool col_ok = active && member < m;
+  const int bm = col_ok ? rec[2 + member] : 0;
+  const int head = hk * G + (idx - member * G);
+  const int64_t pr = ((int64_t)bm * a.n_heads + head) * a.split_stride + a.num_splits + s;
+
+  const int32_t *table_row = a.req_to_token + (int64_t)pool_row * a.table_stride;
+  asm volatile("" ::"s"(P), "s"(table_row), "s"(a.page_shift), "s"(a.max_ctx_len));
+  if (start >= end) {  // a split past this group's prefix: the empty partial
+    if (a.skip_empty) return;
+    if (col_ok) {
+      float4 *op = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) op[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (g == 0) {
+        a.ml_part[pr * 2 + 0] = kNegInf;
+        a.ml_part[pr * 2 + 1] = 0.f;
+      }
+    }
+    return;
+  }
+  const uint16_t *qcol =
+      col_ok ? reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)bm * a.n_heads + head) * D
+             : nullptr;
+  f32x4_t o[8];
+  float m_run, l_tot;
+  attend_mfma<1, false, kRing>(a, s_slot, pool_row, start, end, 0, active, hk, qcol, nullptr,
+                               nullptr, -1, o, m_run, l_tot);
+  if (!col_ok) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float4 *op = reinterpret_cast<float4 *>(a.o_part + pr * D + 32 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    op[2 * i + 0] = make_float4(o[0][i] * inv, o[1][i] * inv, o[2][i] * inv, o[3][i] * inv);
+    op[2 * i + 1] = make_float4(o[4][i] * inv, o[5][i] * inv, o[6][i] * inv, o[7][i] * inv);
+  }
+  if (g == 0) {
+    a.ml_part[pr * 2 + 0] = m_run;
+    a.ml_part[pr * 2 + 1] = l_tot;
+  }
+}
+
+__global__ void __launch_bounds__(256, 2) decode_prefix_mfma_kernel(const PrefixArgs pa) {
+  __shared__ int32_t s_slot[kSlotTile];
+  prefix_mfma_body(pa, s_slot, blockIdx.z, blockIdx.y, blockIdx.x);
+}
+
+// The whole shared-prefix attention in one launch: the groups' shared keys
+// (workgroups 0 .. pfx_blocks - 1, dispatched first: each takes a longer
+// run of keys) and every request's own keys with the new token's K/V write.
+__global__ void __launch_bounds__(256, 2) decode_shared_mfma_kernel(const SharedArgs sh) {
+  __shared__ int32_t s_slot[kSlotTile];
+  int lin = blockIdx.x;
+  if (lin < sh.pfx_blocks) {
+    const int wx = lin % sh.pfx_wx;
+    const int rest = lin / sh.pfx_wx;
+    const int s = rest % sh.pfx.prefix_splits;
+    prefix_mfma_body(sh.pfx, s_slot, rest / sh.pfx.prefix_splits, s, wx);
+  } else {
+    lin -= sh.pfx_blocks;
+    const int wx = lin % sh.sfx_wx;
+    const int rest = lin / sh.sfx_wx;
+    const int s = rest % sh.sfx.d.num_splits;
+    split_mfma_body<true>(sh.sfx, s_slot, rest / sh.sfx.d.num_splits, s, wx);
   }
 }
 
@@ -742,7 +871,10 @@ __global__ void __launch_bounds__(256, 2) decode_step_kernel(const StepArgs sa) 
 
   f32x4_t o[8];
   float m_run, l_tot;
-  attend_mfma<4, true, kRing>(a, s_slot, b, pool_row, start, end, wave, true, hk, h0, c < ng, knew, vnew,
+  const uint16_t *qcol =
+      c < ng ? reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)b * a.n_heads + h0 + c) * D
+             : nullptr;
+  attend_mfma<4, true, kRing>(a, s_slot, pool_row, start, end, wave, true, hk, qcol, knew, vnew,
                               newpos, o, m_run, l_tot);
 
   // Combine the four waves' states into the split partial.
@@ -942,6 +1074,30 @@ hipError_t launch_decode_split_store(const StepArgs &args, hipStream_t stream) {
   a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
   const dim3 grid((a.n_kv_heads * a.n_chunks + 3) / 4, a.num_splits, a.batch);
   hipLaunchKernelGGL(decode_split_mfma_kernel<true>, grid, dim3(256), 0, stream, sa);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_shared(const SharedArgs &args, hipStream_t stream) {
+  SharedArgs sh = args;
+  DecodeArgs &a = sh.sfx.d;
+  a.n_chunks = (a.group + 15) / 16;
+  a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
+  sh.sfx_wx = (a.n_kv_heads * a.n_chunks + 3) / 4;
+  const int n_cc = (sh.pfx.max_members * sh.pfx.d.group + 15) / 16;
+  sh.pfx_wx = (sh.pfx.d.n_kv_heads * n_cc + 3) / 4;
+  const int64_t pfx_blocks = (int64_t)sh.pfx_wx * sh.pfx.prefix_splits * sh.pfx.n_groups;
+  const int64_t blocks = pfx_blocks + (int64_t)sh.sfx_wx * a.num_splits * a.batch;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  sh.pfx_blocks = (int32_t)pfx_blocks;
+  hipLaunchKernelGGL(decode_shared_mfma_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, sh);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_prefix(const PrefixArgs &args, hipStream_t stream) {
+  PrefixArgs pa = args;
+  const int n_cc = (args.max_members * args.d.group + 15) / 16;
+  const dim3 grid((args.d.n_kv_heads * n_cc + 3) / 4, args.prefix_splits, args.n_groups);
+  hipLaunchKernelGGL(decode_prefix_mfma_kernel, grid, dim3(256), 0, stream, pa);
   return hipGetLastError();
 }
 

@@ -59,6 +59,14 @@ struct DecodeArgs {
   int32_t num_splits;
   int32_t chunk;              // tokens per split (multiple of 16)
   float scale_log2;           // sm_scale * log2(e)
+  // Shared-prefix decode (matrix-core split kernel only): request b's splits
+  // cover keys [kv_start[b], seq_lens[b]) (null: from 0), and partial rows
+  // hold split_stride splits (num_splits when no prefix partials follow).
+  const int32_t *kv_start;
+  int32_t split_stride;
+  // Splits with no keys leave their partial unwritten (the merge is told
+  // which splits hold keys); 0: every split writes one.
+  int32_t skip_empty;
 };
 // dtype: 0 = f32, 1 = bf16
 hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
@@ -107,8 +115,49 @@ struct MergeArgs {
   const float *ml_part;
   void *out;                  // [batch, n_heads, head_dim]
   int32_t rows;               // batch * n_heads
-  int32_t num_splits;
+  int32_t num_splits;         // splits of every row
+  // Shared-prefix decode: rows hold `stride` splits; a request with
+  // kv_start[b] > 0 also has prefix_splits prefix partials after its
+  // num_splits own ones (null kv_start: stride == num_splits, none).
+  const int32_t *kv_start;
+  int32_t stride;
+  int32_t n_heads;
+  int32_t prefix_splits;
+  // When not null, only the splits holding keys are read: own splits from
+  // kv_start (or 0) in steps of chunk up to seq_lens, prefix splits in steps
+  // of prefix_chunk below kv_start (lengths past max_ctx_len: all splits).
+  const int32_t *seq_lens;
+  int32_t chunk;
+  int32_t prefix_chunk;
+  int64_t max_ctx_len;
 };
+
+// Shared-prefix decode: a group's members share the slots of their first P
+// positions; the group record (PKV_PREFIX_GROUP_INTS int32 on the device) is
+// [P, m, b_0 .. b_{m-1}].  One launch attends every group's shared keys with
+// the members' query heads as matrix-core columns and writes each member's
+// prefix partials after its own splits.
+struct PrefixArgs {
+  DecodeArgs d;               // chunk: prefix split size; num_splits: the
+                              // members' own splits (prefix partials follow)
+  const int32_t *groups;
+  int32_t n_groups;
+  int32_t prefix_splits;
+  int32_t group_ints;         // int32 per group record
+  int32_t max_members;
+};
+hipError_t launch_decode_prefix(const PrefixArgs &a, hipStream_t stream);
+
+// The shared-prefix attention of one decode step in one launch: prefix
+// workgroups first, then every request's own splits with the K/V write.
+struct SharedArgs {
+  StepArgs sfx;               // own keys from kv_start (d.kv_start set)
+  PrefixArgs pfx;
+  int32_t pfx_wx;             // workgroups per (group, prefix split)  (set by the launcher)
+  int32_t sfx_wx;             // workgroups per (request, split)       (set by the launcher)
+  int32_t pfx_blocks;         // prefix workgroups                      (set by the launcher)
+};
+hipError_t launch_decode_shared(const SharedArgs &a, hipStream_t stream);
 hipError_t launch_decode_merge(const MergeArgs &a, int dtype, int head_dim, hipStream_t stream);
 
 struct PrefillArgs {

@@ -70,6 +70,27 @@ const char *layer_ptr(const void *buf, const pkv_pool *p, int32_t layer_id) {
   return reinterpret_cast<const char *>(buf) + (int64_t)layer_id * p->size * row;
 }
 
+// Merge of split partials that skip_empty split kernels wrote: only the
+// splits holding keys of each request are read (seq_lens, kv_start, chunk).
+pkv::MergeArgs merge_args(const pkv::DecodeArgs &a, void *out, const int32_t *kv_start,
+                          int32_t prefix_splits, int32_t prefix_chunk) {
+  pkv::MergeArgs m{};
+  m.o_part = a.o_part;
+  m.ml_part = a.ml_part;
+  m.out = out;
+  m.rows = a.batch * a.n_heads;
+  m.num_splits = a.num_splits;
+  m.kv_start = kv_start;
+  m.stride = a.split_stride;
+  m.n_heads = a.n_heads;
+  m.prefix_splits = prefix_splits;
+  m.seq_lens = a.seq_lens;
+  m.chunk = a.chunk;
+  m.prefix_chunk = prefix_chunk > 0 ? prefix_chunk : 1;
+  m.max_ctx_len = a.max_ctx_len;
+  return m;
+}
+
 int32_t decode_chunk(int32_t max_len, int32_t num_splits) {
   int64_t c = ((int64_t)max_len + num_splits - 1) / num_splits;
   c = ((c + kSplitAlign - 1) / kSplitAlign) * kSplitAlign;
@@ -262,7 +283,7 @@ pkv_status pkv_kv_store(const pkv_pool *pool, int32_t layer_id, const void *k_ne
   if (!k_new || !v_new || !out_cache_loc) return PKV_ERR_NULL;
   const int64_t row_bytes = (int64_t)pool->n_kv_heads * pool->head_dim * dtype_bytes(pool->dtype);
   if (row_bytes > INT32_MAX) return PKV_ERR_SHAPE;
-  pkv::KvStoreArgs a;
+  pkv::KvStoreArgs a{};
   a.k_layer = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
   a.v_layer = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
   a.k_new = k_new;
@@ -323,7 +344,7 @@ pkv_status pkv_paged_decode(const pkv_pool *pool, int32_t layer_id, const pkv_st
   if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, pool->head_dim, num_splits))
     return PKV_ERR_WORKSPACE_TOO_SMALL;
   const int32_t group = n_heads / pool->n_kv_heads;
-  pkv::DecodeArgs a;
+  pkv::DecodeArgs a{};
   a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
   a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
   set_table(a, pool);
@@ -340,6 +361,9 @@ pkv_status pkv_paged_decode(const pkv_pool *pool, int32_t layer_id, const pkv_st
   a.heads_per_chunk = 0;
   a.num_splits = num_splits;
   a.chunk = decode_chunk(step->max_len, num_splits);
+  a.kv_start = nullptr;
+  a.split_stride = num_splits;
+  a.skip_empty = 0;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   return hip_status(pkv::launch_paged_decode(a, pool->dtype == PKV_BF16 ? 1 : 0,
                                               pool->head_dim, (hipStream_t)stream));
@@ -384,7 +408,7 @@ pkv_status pkv_paged_decode_step(const pkv_pool *pool, int32_t layer_id, const p
     return pkv_paged_decode_merge(step->batch, n_heads, pool->head_dim, pool->dtype, num_splits,
                                   workspace, ws_bytes, out, stream);
   }
-  pkv::StepArgs sa;
+  pkv::StepArgs sa{};
   pkv::DecodeArgs &a = sa.d;
   a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
   a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
@@ -402,6 +426,9 @@ pkv_status pkv_paged_decode_step(const pkv_pool *pool, int32_t layer_id, const p
   a.heads_per_chunk = 0;
   a.num_splits = num_splits;
   a.chunk = decode_chunk(step->max_len, num_splits);
+  a.kv_start = nullptr;
+  a.split_stride = num_splits;
+  a.skip_empty = 0;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   sa.k_new = k_new;
   sa.v_new = v_new;
@@ -456,17 +483,211 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
     a.group = n_heads / pool->n_kv_heads;
     a.num_splits = num_splits;
     a.chunk = decode_chunk(step->max_len, num_splits);
+    a.kv_start = nullptr;
+    a.split_stride = num_splits;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     sa.k_new = k_new;
     sa.v_new = v_new;
     sa.k_layer_w = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
     sa.v_layer_w = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
     sa.out_cache_loc = step->out_cache_loc;
+    // Splits past a request's keys leave no partial; the merge reads only the
+    // ones that hold keys.
+    a.skip_empty = 1;
     st = hip_status(pkv::launch_decode_split_store(sa, (hipStream_t)stream));
     if (st != PKV_OK) return st;
+    pkv::MergeArgs m = merge_args(a, out, nullptr, 0, 0);
+    return hip_status(pkv::launch_decode_merge(m, 1, pool->head_dim, (hipStream_t)stream));
   }
   return pkv_paged_decode_merge(step->batch, n_heads, pool->head_dim, pool->dtype, num_splits,
                                 workspace, ws_bytes, out, stream);
+}
+
+pkv_status pkv_decode_prefix_groups(int32_t batch, const int32_t *req_pool_indices,
+                                    const int32_t *seq_lens, const int32_t *req_to_token,
+                                    int64_t num_reqs, int64_t max_ctx_len, int32_t page_size,
+                                    int32_t min_prefix, int32_t *groups, int64_t groups_cap,
+                                    int64_t *n_groups, int32_t *kv_start, int32_t *max_prefix,
+                                    int32_t *max_members, int32_t *max_suffix) {
+  const int sh = page_shift_of(page_size);
+  if (batch < 0 || sh < 0 || groups_cap < 0) return PKV_ERR_SHAPE;
+  if (!n_groups || !max_prefix || !max_members || !max_suffix) return PKV_ERR_NULL;
+  if (batch > 0 && (!req_pool_indices || !seq_lens || !req_to_token || !kv_start))
+    return PKV_ERR_NULL;
+  if (groups_cap > 0 && !groups) return PKV_ERR_NULL;
+  const int64_t stride = table_stride_of(max_ctx_len, sh);
+  const int64_t ps = int64_t(1) << sh;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t r = req_pool_indices[b];
+    if (r < 0 || r >= num_reqs || seq_lens[b] < 1 || seq_lens[b] > max_ctx_len)
+      return PKV_ERR_BAD_METADATA;
+    kv_start[b] = 0;
+  }
+  const int32_t min_p = std::max(1, min_prefix);
+  auto row = [&](int32_t b) { return req_to_token + (int64_t)req_pool_indices[b] * stride; };
+  // Positions both requests read through the same table entries (their
+  // leading equal entries, in positions), leaving each request's last
+  // position, the one this step writes, out of the shared range.
+  auto shared = [&](int32_t x, int32_t y) -> int64_t {
+    const int64_t cap = (int64_t)std::min(seq_lens[x], seq_lens[y]) - 1;
+    const int32_t *rx = row(x), *ry = row(y);
+    int64_t e = 0;
+    while (e * ps < cap && rx[e] == ry[e]) ++e;
+    return std::min(e * ps, cap);
+  };
+  // Requests whose first table entries agree, in batch order of the first.
+  std::vector<std::vector<int32_t>> buckets;
+  {
+    std::vector<std::pair<int32_t, int32_t>> keyed;   // (first entry, b)
+    for (int32_t b = 0; b < batch; ++b)
+      if (seq_lens[b] >= 2) keyed.push_back({row(b)[0], b});
+    std::stable_sort(keyed.begin(), keyed.end(),
+                     [](const auto &u, const auto &v) { return u.first < v.first; });
+    for (size_t i = 0; i < keyed.size();) {
+      size_t j = i;
+      std::vector<int32_t> mem;
+      while (j < keyed.size() && keyed[j].first == keyed[i].first) mem.push_back(keyed[j++].second);
+      if (mem.size() >= 2) buckets.push_back(mem);
+      i = j;
+    }
+    std::sort(buckets.begin(), buckets.end(),
+              [](const auto &u, const auto &v) { return u[0] < v[0]; });
+  }
+  int64_t ng = 0;
+  int32_t mp = 0, mm = 0;
+  for (auto &pending : buckets) {
+    while (pending.size() >= 2) {
+      // The lead is the longest pending request (earliest on ties): a
+      // request's shared range ends before its own last position, so a short
+      // lead would cut every member's.
+      size_t li = 0;
+      for (size_t i = 1; i < pending.size(); ++i)
+        if (seq_lens[pending[i]] > seq_lens[pending[li]]) li = i;
+      const int32_t lead = pending[li];
+      std::vector<std::pair<int64_t, int32_t>> cand;   // (shared positions with lead, b)
+      for (size_t i = 0; i < pending.size(); ++i)
+        if (i != li) cand.push_back({shared(lead, pending[i]), pending[i]});
+      std::stable_sort(cand.begin(), cand.end(),
+                       [](const auto &u, const auto &v) { return u.first > v.first; });
+      // Members = lead + the k-1 requests sharing the most with it; the
+      // group's prefix is the smallest of their shared ranges.  Pick k for
+      // the most positions read once instead of k times.
+      int64_t best = 0;
+      size_t best_k = 0;
+      for (size_t k = 2; k <= std::min<size_t>(cand.size() + 1, PKV_PREFIX_GROUP_MAX); ++k) {
+        const int64_t P = cand[k - 2].first;
+        if (P < min_p) break;
+        const int64_t gain = (int64_t)(k - 1) * P;
+        if (gain > best) {
+          best = gain;
+          best_k = k;
+        }
+      }
+      if (best_k == 0) {  // the lead shares too little with anyone: it stays alone
+        pending.erase(pending.begin() + li);
+        continue;
+      }
+      const int32_t P = (int32_t)cand[best_k - 2].first;
+      if (ng >= groups_cap) return PKV_ERR_SHAPE;
+      int32_t *rec = groups + ng * PKV_PREFIX_GROUP_INTS;
+      for (int i = 0; i < PKV_PREFIX_GROUP_INTS; ++i) rec[i] = 0;
+      rec[0] = P;
+      rec[1] = (int32_t)best_k;
+      rec[2] = lead;
+      kv_start[lead] = P;
+      std::vector<int32_t> taken{lead};
+      for (size_t i = 0; i + 1 < best_k; ++i) {
+        rec[3 + i] = cand[i].second;
+        kv_start[cand[i].second] = P;
+        taken.push_back(cand[i].second);
+      }
+      ++ng;
+      mp = std::max(mp, P);
+      mm = std::max(mm, (int32_t)best_k);
+      std::vector<int32_t> rest;
+      for (int32_t b : pending)
+        if (std::find(taken.begin(), taken.end(), b) == taken.end()) rest.push_back(b);
+      pending.swap(rest);
+    }
+  }
+  int32_t msfx = 0;
+  for (int32_t b = 0; b < batch; ++b) msfx = std::max(msfx, seq_lens[b] - kv_start[b]);
+  *n_groups = ng;
+  *max_prefix = mp;
+  *max_members = mm;
+  *max_suffix = msfx;
+  return PKV_OK;
+}
+
+pkv_status pkv_paged_decode_shared(const pkv_pool *pool, int32_t layer_id, const pkv_step *step,
+                                   const pkv_prefix_groups *pg, const void *q, const void *k_new,
+                                   const void *v_new, int32_t n_heads, float sm_scale,
+                                   int32_t num_splits, int32_t prefix_splits, void *workspace,
+                                   size_t ws_bytes, void *out, void *stream) {
+  pkv_status st = check_pool(pool, layer_id);
+  if (st != PKV_OK) return st;
+  if (!step || !q || !workspace || !out) return PKV_ERR_NULL;
+  if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || num_splits <= 0 ||
+      num_splits > 65535 || step->batch > 65535)
+    return PKV_ERR_SHAPE;
+  const bool mfma = pool->dtype == PKV_BF16 && pool->head_dim == 128;
+  if (!pg || pg->n_groups <= 0 || !mfma)  // nothing shared, or no matrix-core path: plain step
+    return pkv_paged_decode_store(pool, layer_id, step, q, k_new, v_new, n_heads, sm_scale,
+                                  num_splits, workspace, ws_bytes, out, stream);
+  if (!std::isfinite(sm_scale)) return PKV_ERR_SHAPE;
+  if (step->batch == 0) return PKV_OK;
+  if (!k_new || !v_new || !step->out_cache_loc || !step->req_pool_indices || !step->seq_lens ||
+      !pg->groups || !pg->kv_start)
+    return PKV_ERR_NULL;
+  if (step->n_new != step->batch) return PKV_ERR_SHAPE;
+  if (prefix_splits <= 0 || prefix_splits > 65535 || pg->n_groups > 65535 ||
+      pg->max_members < 1 || pg->max_members > PKV_PREFIX_GROUP_MAX || pg->max_prefix < 1 ||
+      pg->max_suffix < 1 || pg->max_prefix > pool->max_ctx_len ||
+      pg->max_suffix > pool->max_ctx_len || (int64_t)num_splits + prefix_splits > 65535)
+    return PKV_ERR_SHAPE;
+  const int32_t total = num_splits + prefix_splits;
+  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, pool->head_dim, total))
+    return PKV_ERR_WORKSPACE_TOO_SMALL;
+  pkv::DecodeArgs a{};
+  a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
+  a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
+  set_table(a, pool);
+  a.req_pool_indices = step->req_pool_indices;
+  a.seq_lens = step->seq_lens;
+  a.q = q;
+  a.o_part = reinterpret_cast<float *>(workspace);
+  a.ml_part = a.o_part + (size_t)step->batch * n_heads * total * pool->head_dim;
+  a.batch = step->batch;
+  a.n_heads = n_heads;
+  a.n_kv_heads = pool->n_kv_heads;
+  a.group = n_heads / pool->n_kv_heads;
+  a.num_splits = num_splits;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.split_stride = total;
+  a.skip_empty = 1;
+  // the groups' shared keys, once per group, and every request's own keys
+  // from kv_start[b] with the new token's K/V write: one launch
+  pkv::SharedArgs sh{};
+  sh.pfx.d = a;
+  sh.pfx.d.chunk = decode_chunk(pg->max_prefix, prefix_splits);
+  sh.pfx.d.kv_start = nullptr;
+  sh.pfx.groups = pg->groups;
+  sh.pfx.n_groups = pg->n_groups;
+  sh.pfx.prefix_splits = prefix_splits;
+  sh.pfx.group_ints = PKV_PREFIX_GROUP_INTS;
+  sh.pfx.max_members = pg->max_members;
+  sh.sfx.d = a;
+  sh.sfx.d.chunk = decode_chunk(pg->max_suffix, num_splits);
+  sh.sfx.d.kv_start = pg->kv_start;
+  sh.sfx.k_new = k_new;
+  sh.sfx.v_new = v_new;
+  sh.sfx.k_layer_w = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
+  sh.sfx.v_layer_w = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
+  sh.sfx.out_cache_loc = step->out_cache_loc;
+  st = hip_status(pkv::launch_decode_shared(sh, (hipStream_t)stream));
+  if (st != PKV_OK) return st;
+  pkv::MergeArgs m = merge_args(sh.sfx.d, out, pg->kv_start, prefix_splits, sh.pfx.d.chunk);
+  return hip_status(pkv::launch_decode_merge(m, 1, pool->head_dim, (hipStream_t)stream));
 }
 
 pkv_status pkv_decode_advance(const pkv_pool *pool, int32_t batch, const int32_t *req_pool_indices,
@@ -477,7 +698,7 @@ pkv_status pkv_decode_advance(const pkv_pool *pool, int32_t batch, const int32_t
   if (batch < 0) return PKV_ERR_SHAPE;
   if (batch == 0) return PKV_OK;
   if (!req_pool_indices || !seq_lens || !out_cache_loc) return PKV_ERR_NULL;
-  pkv::AdvanceArgs a;
+  pkv::AdvanceArgs a{};
   set_table(a, pool);
   a.req_pool_indices = req_pool_indices;
   a.seq_lens = seq_lens;
@@ -505,7 +726,7 @@ pkv_status pkv_rope_kv_store(const pkv_pool *pool, int32_t layer_id, const void 
   if (!aligned(q) || !aligned(q_out) || !aligned(k_new) || !aligned(v_new) || !aligned(freqs_cis))
     return PKV_ERR_SHAPE;
   if (n_new > INT32_MAX) return PKV_ERR_SHAPE;
-  pkv::RopeArgs a;
+  pkv::RopeArgs a{};
   a.q = q;
   a.q_out = q_out;
   a.k_new = k_new;
@@ -534,12 +755,16 @@ pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_d
   if (batch == 0) return PKV_OK;
   if (ws_bytes < pkv_decode_workspace_bytes(batch, n_heads, head_dim, num_splits))
     return PKV_ERR_WORKSPACE_TOO_SMALL;
-  pkv::MergeArgs a;
+  pkv::MergeArgs a{};
   a.o_part = reinterpret_cast<const float *>(workspace);
   a.ml_part = a.o_part + (size_t)batch * n_heads * num_splits * head_dim;
   a.out = out;
   a.rows = batch * n_heads;
   a.num_splits = num_splits;
+  a.kv_start = nullptr;
+  a.stride = num_splits;
+  a.n_heads = n_heads;
+  a.prefix_splits = 0;
   return hip_status(pkv::launch_decode_merge(a, out_dtype == PKV_BF16 ? 1 : 0, head_dim,
                                              (hipStream_t)stream));
 }
@@ -559,7 +784,7 @@ pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_s
   if (step->batch == 0 || step->n_new == 0) return PKV_OK;
   if (!step->req_pool_indices || !step->qo_indptr || !step->kv_indptr) return PKV_ERR_NULL;
   if (step->max_q_len <= 0 || step->max_q_len > pool->max_ctx_len) return PKV_ERR_SHAPE;
-  pkv::PrefillArgs a;
+  pkv::PrefillArgs a{};
   a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
   a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
   set_table(a, pool);
