@@ -50,12 +50,7 @@ constexpr int WROWS = 32;            // query rows per wavefront
 constexpr int BM = NT / 64 * WROWS;  // query rows per workgroup
 static_assert(BM == kPrefillBlockRows, "row block size");
 constexpr int NBUF = 3;              // LDS tile buffers
-// A tile's weights are first taken against the running reference as it
-// stands; only when this lane's sum of them exceeds kTileSumMax (or is not
-// finite) is the reference raised to the tile's maximum and the weights
-// recomputed.  Each weight is at most the sum, so weights stay <= 2^16 and
-// the fp32 running sums far from overflow.
-constexpr float kTileSumMax = 65536.f;
+constexpr float kSlack = 8.f;        // log2 headroom before the running max is raised
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) {
   return __builtin_bit_cast(bf16x8_t, v);
@@ -239,14 +234,16 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
     for (int x = 0; x < 16; ++x) o[db][x] = 0.f;
-  // Running reference in raw score units (sm_scale > 0 keeps the order) and
-  // this lane's share of the running sum (its half of the keys).
+  // Running max in raw score units (sm_scale > 0 keeps the order), the raw
+  // score above which it must move, and this lane's share of the running sum
+  // (its half of the keys).
   // Transposed V reads: lane l of 16-lane group g addresses key (l%16)/4 of
   // its 4-key run, dims 16(g&1) + 4(l%4) .. +3 of the 32-dim block.
   const int gl = lane & 15;
   const int voff = 16 * ((lane >> 4) & 1) + 4 * (gl & 3);
   const float c2 = a.scale_log2;
-  float m_run = kNegInf, l_lane = 0.f;
+  const float slack_raw = kSlack / c2;
+  float m_run = kNegInf, m_thr = kNegInf, l_lane = 0.f;
   const f32x16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                            0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
@@ -267,30 +264,6 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  // The tile's softmax weights against reference mc (base-2 units), rounded
-  // to bf16 (one 16-key step per pf entry), and this lane's sum of them.
-  auto weights = [&](const f32x16_t(&sacc)[2], float mc, uint4(&pf)[4]) __attribute__((always_inline)) {
-    float tsum = 0.f;
-#pragma unroll
-    for (int ts = 0; ts < 4; ++ts) {
-      const int kb = ts >> 1;
-      const int x0 = 8 * (ts & 1);
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(sacc[kb][x0 + e], c2, -mc));
-      pf[ts].x = pack_bf16x2(p[0], p[1]);
-      pf[ts].y = pack_bf16x2(p[2], p[3]);
-      pf[ts].z = pack_bf16x2(p[4], p[5]);
-      pf[ts].w = pack_bf16x2(p[6], p[7]);
-      // the row sum uses the same bf16 weights the PV product sees
-      tsum = dot2_bf16(pf[ts].x, kOnes, tsum);
-      tsum = dot2_bf16(pf[ts].y, kOnes, tsum);
-      tsum = dot2_bf16(pf[ts].z, kOnes, tsum);
-      tsum = dot2_bf16(pf[ts].w, kOnes, tsum);
-    }
-    return tsum;
-  };
-
   // (Mask,) online softmax of one tile's S^T, then O^T += V^T P^T.
   auto softmax_pv = [&](int tile, f32x16_t(&sacc)[2], const Smem<D> &buf,
                         auto masked) __attribute__((always_inline)) {
@@ -303,38 +276,54 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
         for (int x = 0; x < 16; ++x)
           if (kbase_idx + kb * 32 + 8 * (x >> 2) + (x & 3) >= lim) sacc[kb][x] = kNegInf;
     }
-    // Weights against the reference as it stands.  Numerator and denominator
-    // share the reference, so any reference gives the same function; only a
-    // weight sum out of range (or not finite: the first tile, where the
-    // reference is -inf) makes the reference move.
-    uint4 pf[4];
-    float tsum = weights(sacc, m_run == kNegInf ? 0.f : m_run * c2, pf);
-    if (__any(!(tsum <= kTileSumMax))) {
-      // Max over this lane's half of the row (32 of the tile's 64 keys): a
-      // tree of three-input maxes, then the other half's through lane l ^ 32.
-      auto max3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
-      float m11[11];
+    // Max over this lane's half of the row (32 of the tile's 64 keys): a
+    // tree of three-input maxes, 17 instructions at depth 4.
+    auto max3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
+    float m11[11];
 #pragma unroll
-      for (int j = 0; j < 10; ++j) {
-        const int e = 3 * j;
-        m11[j] = max3(sacc[e >> 4][e & 15], sacc[(e + 1) >> 4][(e + 1) & 15],
-                      sacc[(e + 2) >> 4][(e + 2) & 15]);
-      }
-      m11[10] = fmaxf(sacc[1][14], sacc[1][15]);
-      const float tmax = fmaxf(max3(max3(m11[0], m11[1], m11[2]), max3(m11[3], m11[4], m11[5]),
-                                    max3(m11[6], m11[7], m11[8])),
-                               fmaxf(m11[9], m11[10]));
+    for (int j = 0; j < 10; ++j) {
+      const int e = 3 * j;
+      m11[j] = max3(sacc[e >> 4][e & 15], sacc[(e + 1) >> 4][(e + 1) & 15],
+                    sacc[(e + 2) >> 4][(e + 2) & 15]);
+    }
+    m11[10] = fmaxf(sacc[1][14], sacc[1][15]);
+    const float tmax = fmaxf(max3(max3(m11[0], m11[1], m11[2]), max3(m11[3], m11[4], m11[5]),
+                                  max3(m11[6], m11[7], m11[8])),
+                             fmaxf(m11[9], m11[10]));
+    // The reference max only moves when a score exceeds it by more than
+    // 2^kSlack in weight; below that, weights up to 2^kSlack accumulate
+    // against the old reference (exact: numerator and denominator share it),
+    // so the O rescale is rare after the first tiles.  Each half of the wave
+    // tests its own keys; only a move needs the row max over both halves.
+    if (__any(tmax > m_thr)) {
       const float m_new = fmaxf(m_run, fmaxf(tmax, __shfl_xor(tmax, 32)));
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run - m_new) * c2);
       l_lane *= alpha;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
       m_run = m_new;
-      tsum = weights(sacc, m_run == kNegInf ? 0.f : m_run * c2, pf);
+      m_thr = m_new + slack_raw;
     }
-    l_lane += tsum;
+    const float mc = (m_run == kNegInf) ? 0.f : m_run * c2;
+    // Per 16-key step: weights for those keys, rounded to bf16, then the PV
+    // products that consume them.
 #pragma unroll
     for (int ts = 0; ts < 4; ++ts) {
+      const int kb = ts >> 1;
+      const int x0 = 8 * (ts & 1);
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(sacc[kb][x0 + e], c2, -mc));
+      uint4 pf;
+      pf.x = pack_bf16x2(p[0], p[1]);
+      pf.y = pack_bf16x2(p[2], p[3]);
+      pf.z = pack_bf16x2(p[4], p[5]);
+      pf.w = pack_bf16x2(p[6], p[7]);
+      // the row sum uses the same bf16 weights the PV product sees
+      l_lane = dot2_bf16(pf.x, kOnes, l_lane);
+      l_lane = dot2_bf16(pf.y, kOnes, l_lane);
+      l_lane = dot2_bf16(pf.z, kOnes, l_lane);
+      l_lane = dot2_bf16(pf.w, kOnes, l_lane);
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
         // V^T operand: keys 16ts + 4half + {0..3} and 16ts + 8 + 4half + {0..3}
@@ -342,7 +331,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
         const uint16_t *vb = &buf.v[(16 * ts + 4 * half + (gl >> 2)) * VS + db * 32 + voff];
         const uint2 lo = lds_read_tr16(vb);
         const uint2 hi = lds_read_tr16(vb + 8 * VS);
-        o[db] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[ts], o[db]);
+        o[db] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf, o[db]);
       }
     }
   };
@@ -369,19 +358,6 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   int cur = 0;   // buffer of tile k
   int prev = 2;  // buffer of tile k-1
   auto next_buf = [](int b) { return b == NBUF - 1 ? 0 : b + 1; };
-  // A wavefront whose 32 rows all lie past the request's last row (in the
-  // request's last row block) only stages tiles and passes the barriers, so
-  // the wavefront sharing its SIMD runs alone.
-  if (rb * BM + wave * WROWS >= rows) {
-    for (int k = 0; k < ntiles; ++k) {
-      const int nb = next_buf(cur);
-      stash(sm[nb]);
-      fetch(k + 2);
-      lds_barrier();
-      cur = nb;
-    }
-    return;
-  }
   if (wave < 4) {
     auto period = [&](int k, auto masked) __attribute__((always_inline)) {
       const int nb = next_buf(cur);
