@@ -24,5 +24,6 @@ from .attention import (  # noqa: F401
     split_partial,
     validate_step,
 )
-from .rope import round_to_bf16, rope_kv_store, rope_rotate, to_dtype  # noqa: F401
+from .rope import (  # noqa: F401
+    round_to_bf16, rope_kv_store, rope_rotate, rope_rotate_tail, to_dtype)
 from . import pages  # noqa: F401,E402  (pools of page_size > 1 tokens)

@@ -203,12 +203,14 @@ def decode(k_buffer, v_buffer, layer_id, req_to_token, req_pool_indices,
            seq_lens, q, sm_scale) -> np.ndarray:
     """Decode attention: one query row per request and head, attending to all
     seq_len cached keys of that request (the just-written token included),
-    gathered through req_to_token.  q [B, H, d] -> out [B, H, d] fp64."""
+    gathered through req_to_token.  q [B, H, dk] -> out [B, H, dv] fp64, dv the
+    width of the value rows (keys and queries share dk)."""
     q = _f64(q)
-    B, H, d = q.shape
+    B, H, _ = q.shape
     Hk = k_buffer.shape[2]
     G = H // Hk
-    out = np.zeros((B, H, d), dtype=np.float64)
+    dv = v_buffer.shape[3]   # outputs have the value rows' width
+    out = np.zeros((B, H, dv), dtype=np.float64)
     for b in range(B):
         r = int(req_pool_indices[b])
         L = int(seq_lens[b])
@@ -237,7 +239,7 @@ def decode_pairs(k_buffer, v_buffer, layer_id, req_to_token, req_pool_indices,
         K = _gather(k_buffer, layer_id, slots, hk)
         V = _gather(v_buffer, layer_id, slots, hk)
         rows.append(attend(q[b, h], K, V, sm_scale)[0])
-    return np.stack(rows) if rows else np.zeros((0, q.shape[2]))
+    return np.stack(rows) if rows else np.zeros((0, v_buffer.shape[3]))
 
 
 # ---------------------------------------------------------------------------
@@ -288,10 +290,11 @@ def decode_split(k_buffer, v_buffer, layer_id, req_to_token, req_pool_indices,
     seq_len_b] for request b; split s covers logical keys [e_s, e_{s+1}).
     Mathematically equal to decode(); used to pin split independence."""
     q = _f64(q)
-    B, H, d = q.shape
+    B, H, _ = q.shape
     Hk = k_buffer.shape[2]
     G = H // Hk
-    out = np.zeros((B, H, d), dtype=np.float64)
+    dv = v_buffer.shape[3]   # outputs have the value rows' width
+    out = np.zeros((B, H, dv), dtype=np.float64)
     for b in range(B):
         r = int(req_pool_indices[b])
         L = int(seq_lens[b])
@@ -329,7 +332,7 @@ def prefill_rows(k_buffer, v_buffer, layer_id, req_to_token, req_pool_indices,
     G = H // Hk
     qo = [int(x) for x in qo_indptr]
     rows = [(int(tok), int(h)) for tok, h in rows]
-    out = np.zeros((len(rows), q.shape[2]), dtype=np.float64)
+    out = np.zeros((len(rows), v_buffer.shape[3]), dtype=np.float64)
     groups = {}
     for n, (tok, h) in enumerate(rows):
         i = int(np.searchsorted(qo, tok, side="right")) - 1
@@ -354,16 +357,17 @@ def prefill_rows(k_buffer, v_buffer, layer_id, req_to_token, req_pool_indices,
 def prefill(k_buffer, v_buffer, layer_id, req_to_token, req_pool_indices,
             seq_lens, qo_indptr, q, sm_scale, causal: bool = True,
             row_block: int = 512) -> np.ndarray:
-    """Prefill output for every new token and head: q [n_new, H, d] -> [n_new, H, d].
+    """Prefill output for every new token and head: q [n_new, H, dk] -> [n_new, H, dv].
 
     Per request and head, the gathered K/V rows are shared by all of that
     request's new tokens; each row keeps its own visible-key count.  Rows are
     evaluated in groups of row_block only to bound memory."""
     q = _f64(q)
-    n_new, H, d = q.shape
+    n_new, H, _ = q.shape
     Hk = k_buffer.shape[2]
     G = H // Hk
-    out = np.zeros((n_new, H, d), dtype=np.float64)
+    dv = v_buffer.shape[3]   # outputs have the value rows' width
+    out = np.zeros((n_new, H, dv), dtype=np.float64)
     B = len(seq_lens)
     for i in range(B):
         r = int(req_pool_indices[i])

@@ -129,14 +129,15 @@ def write(k_buffer: np.ndarray, v_buffer: np.ndarray, layer_id: int, page_table:
 def decode(k_buffer, v_buffer, layer_id, page_table, page_size, req_pool_indices, seq_lens,
            q, sm_scale) -> np.ndarray:
     """Decode over a paged pool: each request's query rows attend its seq_len
-    positions gathered page by page.  q [B, H, d] -> [B, H, d] fp64."""
+    positions gathered page by page.  q [B, H, dk] -> [B, H, dv] fp64 (dv: the
+    value rows' width)."""
     q = _f64(q)
-    B, H, d = q.shape
+    B, H, _ = q.shape
     Hk = k_buffer.shape[2]
     G = H // Hk
     k5 = page_view(k_buffer, page_size)
     v5 = page_view(v_buffer, page_size)
-    out = np.zeros((B, H, d), dtype=np.float64)
+    out = np.zeros((B, H, v_buffer.shape[3]), dtype=np.float64)
     for b in range(B):
         row = page_table[int(req_pool_indices[b])]
         L = int(seq_lens[b])
@@ -164,21 +165,21 @@ def decode_pairs(k_buffer, v_buffer, layer_id, page_table, page_size, req_pool_i
         K = gather_rows(k5, layer_id, row, L, h // G)
         V = gather_rows(v5, layer_id, row, L, h // G)
         rows.append(attend(q[b, h], K, V, sm_scale)[0])
-    return np.stack(rows) if rows else np.zeros((0, q.shape[2]))
+    return np.stack(rows) if rows else np.zeros((0, v_buffer.shape[3]))
 
 
 def prefill(k_buffer, v_buffer, layer_id, page_table, page_size, req_pool_indices, seq_lens,
             qo_indptr, q, sm_scale, causal: bool = True) -> np.ndarray:
     """Ragged prefill over a paged pool: new token t of request i (prefix
     p_i = seq_len_i - q_len_i) attends positions 0 .. p_i + t when causal,
-    else all seq_len_i positions.  q [n_new, H, d] -> [n_new, H, d] fp64."""
+    else all seq_len_i positions.  q [n_new, H, dk] -> [n_new, H, dv] fp64."""
     q = _f64(q)
-    n_new, H, d = q.shape
+    n_new, H, _ = q.shape
     Hk = k_buffer.shape[2]
     G = H // Hk
     k5 = page_view(k_buffer, page_size)
     v5 = page_view(v_buffer, page_size)
-    out = np.zeros((n_new, H, d), dtype=np.float64)
+    out = np.zeros((n_new, H, v_buffer.shape[3]), dtype=np.float64)
     for i in range(len(seq_lens)):
         row = page_table[int(req_pool_indices[i])]
         L = int(seq_lens[i])
@@ -217,7 +218,7 @@ def prefill_rows(k_buffer, v_buffer, layer_id, page_table, page_size, req_pool_i
         K = gather_rows(k5, layer_id, row, nk, h // G)
         V = gather_rows(v5, layer_id, row, nk, h // G)
         out.append(attend(q[tok, h], K, V, sm_scale)[0])
-    return np.stack(out) if out else np.zeros((0, q.shape[2]))
+    return np.stack(out) if out else np.zeros((0, v_buffer.shape[3]))
 
 
 def validate_step(size: int, page_size: int, page_table: np.ndarray, req_pool_indices,

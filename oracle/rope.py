@@ -17,9 +17,17 @@ Sources (AstrAI project pages):
   * "Inference" guide, section "KVCache System": the write is
     buffer[layer, out_cache_loc] = k.
 
+  * Compare page v1.3.3 -> v1.3.4, class MLA: its queries and keys have
+    qk_nope_head_dim + qk_rope_head_dim dims and its values their own width;
+    only the qk_rope part carries the rotation.
+
 Readings where the pages are silent:
   * The table is an input; how it was filled (base frequency) is not part of
     this step.
+  * MLA rows: the rotated (qk_rope) part is the last qk_rope_head_dim dims of
+    each query and key row, after the qk_nope part (the order the class lists
+    them); its pairs are (2j, 2j+1) counted within that part, and the table
+    is [max_len, qk_rope_head_dim / 2, 2].  The qk_nope dims pass unchanged.
   * The rotated values are rounded once to the pool dtype (bf16: round to
     nearest, ties to even, from the exact fp64 value).
 """
@@ -87,18 +95,36 @@ def to_dtype(x, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def rope_rotate_tail(x, positions: Sequence[int], freqs_cis, rope_dim: int) -> np.ndarray:
+    """MLA rows (class MLA): the last rope_dim dims of every head row are
+    rotated as rope_rotate does a whole row (pairs counted within that part,
+    freqs_cis [max_pos, rope_dim/2, 2]); the first d - rope_dim dims are
+    returned unchanged.  Returns fp64 [n, heads, d]."""
+    x = _f64(x)
+    d = x.shape[2]
+    assert 0 < rope_dim <= d and rope_dim % 2 == 0
+    out = x.copy()
+    out[:, :, d - rope_dim:] = rope_rotate(x[:, :, d - rope_dim:], positions, freqs_cis)
+    return out
+
+
 def rope_kv_store(k_buffer, v_buffer, layer_id: int, out_cache_loc: Sequence[int], q, k_new,
-                  v_new, positions: Sequence[int], freqs_cis, dtype: str):
+                  v_new, positions: Sequence[int], freqs_cis, dtype: str, rope_dim=None):
     """The rotary step of one forward fused with its K/V write ("KV Cache":
     rotate first, then write).
 
     Returns (q_rot, k_pool, v_pool): the rotated queries rounded to ``dtype``,
     and copies of both pools (fp64 values) in which slot out_cache_loc[i] of
     layer layer_id holds the rotated, rounded key row i and the unrotated
-    value row i.  Nothing else changes.
+    value row i.  Nothing else changes.  With rope_dim (MLA rows), only the
+    last rope_dim dims of each query and key row are rotated.
     """
-    q_rot = to_dtype(rope_rotate(q, positions, freqs_cis), dtype)
-    k_rot = to_dtype(rope_rotate(k_new, positions, freqs_cis), dtype)
+    if rope_dim is None:
+        q_rot = to_dtype(rope_rotate(q, positions, freqs_cis), dtype)
+        k_rot = to_dtype(rope_rotate(k_new, positions, freqs_cis), dtype)
+    else:
+        q_rot = to_dtype(rope_rotate_tail(q, positions, freqs_cis, rope_dim), dtype)
+        k_rot = to_dtype(rope_rotate_tail(k_new, positions, freqs_cis, rope_dim), dtype)
     k_out = _f64(k_buffer).copy()
     v_out = _f64(v_buffer).copy()
     v_new = _f64(v_new)

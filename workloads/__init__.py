@@ -48,6 +48,13 @@ class Case:
     # size / page_size pages, and poison_slot is unused (poison_page instead).
     page_size: int = 1
     poison_page: Optional[int] = None
+    # Width of the value rows when it differs from the key rows (MLA-shaped
+    # layers: keys qk_nope + qk_rope wide, values v_head_dim); None: head_dim.
+    v_head_dim: Optional[int] = None
+
+    @property
+    def dv(self) -> int:
+        return int(self.v_head_dim or self.head_dim)
 
     @property
     def batch(self) -> int:
@@ -100,7 +107,7 @@ def random_case(seed: int, seq_lens: Sequence[int], q_lens: Optional[Sequence[in
                 dtype: str = "f32", size: Optional[int] = None, n_layers: int = 1,
                 layer_id: int = 0, num_reqs: Optional[int] = None,
                 max_ctx_len: Optional[int] = None, k_scale: float = 1.0,
-                name: str = "random") -> Case:
+                name: str = "random", v_head_dim: Optional[int] = None) -> Case:
     """Requests with the given lengths; each request's logical positions map to
     distinct slots drawn from one random permutation of the pool; request rows
     are a random subset of num_reqs table rows; unused table entries point at a
@@ -129,7 +136,8 @@ def random_case(seed: int, seq_lens: Sequence[int], q_lens: Optional[Sequence[in
     return Case(name=name, dtype=dtype, n_heads=n_heads, n_kv_heads=n_kv_heads,
                 head_dim=head_dim, n_layers=n_layers, layer_id=layer_id, size=size,
                 req_to_token=table, req_pool_indices=rows, seq_lens=seq_lens,
-                q_lens=q_lens, seed=seed, k_scale=k_scale, poison_slot=poison)
+                q_lens=q_lens, seed=seed, k_scale=k_scale, poison_slot=poison,
+                v_head_dim=v_head_dim)
 
 
 def random_paged_case(seed: int, seq_lens: Sequence[int], page_size: int,
@@ -138,7 +146,7 @@ def random_paged_case(seed: int, seq_lens: Sequence[int], page_size: int,
                       n_pages: Optional[int] = None, n_layers: int = 1, layer_id: int = 0,
                       num_reqs: Optional[int] = None, max_pages: Optional[int] = None,
                       shared_pages: int = 0, k_scale: float = 1.0,
-                      name: str = "random_paged") -> Case:
+                      name: str = "random_paged", v_head_dim: Optional[int] = None) -> Case:
     """Requests with the given lengths on a pool of n_pages pages of page_size
     tokens.  Each request's logical pages map to distinct physical pages taken
     in order from one random permutation of the pages, except that the first
@@ -176,7 +184,7 @@ def random_paged_case(seed: int, seq_lens: Sequence[int], page_size: int,
                 head_dim=head_dim, n_layers=n_layers, layer_id=layer_id,
                 size=n_pages * page_size, req_to_token=table, req_pool_indices=rows,
                 seq_lens=seq_lens, q_lens=q_lens, seed=seed, k_scale=k_scale,
-                page_size=page_size, poison_page=poison)
+                page_size=page_size, poison_page=poison, v_head_dim=v_head_dim)
 
 
 def contiguous_case(seed: int, seq_lens: Sequence[int], max_seq_len: int, **kw) -> Case:
@@ -367,7 +375,7 @@ def make_tensors(case: Case, device="cpu", poison: bool = True) -> Dict[str, obj
     gen.manual_seed(case.seed * 7919 + 17)
     shape = (case.n_layers, case.size, case.n_kv_heads, case.head_dim)
     kb = torch.empty(shape, dtype=dt, device=device)
-    vb = torch.empty(shape, dtype=dt, device=device)
+    vb = torch.empty(shape[:3] + (case.dv,), dtype=dt, device=device)
     if poison and case.n_layers > 1:
         kb.fill_(float("nan"))
         vb.fill_(float("nan"))
@@ -378,7 +386,7 @@ def make_tensors(case: Case, device="cpu", poison: bool = True) -> Dict[str, obj
         # every page no request reads and in the unused tail of each
         # request's last page.
         ps = case.page_size
-        kv5 = [x[case.layer_id].view(case.size // ps, ps, case.n_kv_heads, case.head_dim)
+        kv5 = [x[case.layer_id].view(case.size // ps, ps, case.n_kv_heads, x.shape[-1])
                for x in (kb, vb)]
         keep = torch.zeros(case.size // ps, dtype=torch.bool)
         keep[torch.from_numpy(case.referenced_pages())] = True
@@ -402,7 +410,7 @@ def make_tensors(case: Case, device="cpu", poison: bool = True) -> Dict[str, obj
     n_new = int(case.q_lens.sum())
     q = torch.empty((n_new, case.n_heads, case.head_dim), dtype=dt, device=device)
     k_new = torch.empty((n_new, case.n_kv_heads, case.head_dim), dtype=dt, device=device)
-    v_new = torch.empty((n_new, case.n_kv_heads, case.head_dim), dtype=dt, device=device)
+    v_new = torch.empty((n_new, case.n_kv_heads, case.dv), dtype=dt, device=device)
     _fill_normal(q, gen)
     _fill_normal(k_new, gen, case.k_scale)
     _fill_normal(v_new, gen)
@@ -425,6 +433,21 @@ def rope_table(max_pos: int, head_dim: int, base: float = 10000.0, device="cpu")
     ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
     t = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
     return torch.from_numpy(t).to(device)
+
+
+def mla_decode(seed: int = 6, seq_lens: Sequence[int] = (4096, 1000, 7000, 333),
+               n_heads: int = 16, n_kv_heads: int = 16, qk_nope: int = 128, qk_rope: int = 64,
+               v_head_dim: int = 128, q_lens: Optional[Sequence[int]] = None) -> Case:
+    """An MLA-shaped layer (class MLA of the v1.3.4 compare page): per-head
+    keys of qk_nope + qk_rope dims and values of v_head_dim, in a one-token
+    page pool with random slots; decode unless q_lens are given."""
+    total = int(np.sum(seq_lens))
+    c = random_case(seed, list(seq_lens), q_lens, n_heads=n_heads, n_kv_heads=n_kv_heads,
+                    head_dim=qk_nope + qk_rope, dtype="bf16", size=total + 64,
+                    name="mla_decode" if q_lens is None else "mla_prefill",
+                    v_head_dim=v_head_dim)
+    c.notes.update({"qk_nope_head_dim": qk_nope, "qk_rope_head_dim": qk_rope})
+    return c
 
 
 def named_cases() -> List[str]:
