@@ -32,9 +32,11 @@
  *     prefix sums) is undefined behaviour unless pkv_validate_step accepted
  *     a host copy of it first.
  *   - Offsets into the pool are computed in 64-bit arithmetic.
- *   - Supported: head_dim 64 or 128; dtype f32 or bf16 (prefill: bf16 only);
- *     n_heads a multiple of n_kv_heads; page_size 1 or a power of two up to
- *     65536.
+ *   - Supported: key / value widths (head_dim, v_head_dim) of (64, 64) or
+ *     (128, 128), and MLA-shaped (192, 128) in bf16; dtype f32 or bf16
+ *     (prefill: bf16 only); n_heads a multiple of n_kv_heads; page_size 1 or
+ *     a power of two up to 65536.  Queries are head_dim wide, attention
+ *     outputs and decode partials v_head_dim wide.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -88,6 +90,12 @@ typedef struct {
   int32_t head_dim;
   pkv_dtype dtype;
   int32_t page_size;            /* tokens per page; 0 and 1 both mean one token   */
+  int32_t v_head_dim;           /* width of the value rows; 0 means head_dim.  An
+                                   MLA-shaped layer (v1.3.3 -> v1.3.4 compare page,
+                                   class MLA) has keys of qk_nope_head_dim +
+                                   qk_rope_head_dim = head_dim dims and values of
+                                   v_head_dim: v_buffer is then
+                                   [n_layers, size, n_kv_heads, v_head_dim]      */
 } pkv_pool;
 
 /* One step's KVCache metadata (same section).  Arrays are device pointers;
@@ -338,6 +346,23 @@ pkv_status pkv_rope_kv_store(const pkv_pool *pool, int32_t layer_id, const void 
                              const int32_t *position_ids, const float *freqs_cis,
                              int64_t max_pos, const int32_t *out_cache_loc, int64_t n_new,
                              void *stream);
+
+/* The same write for MLA-shaped layers (v1.3.3 -> v1.3.4 compare page, class
+ * MLA: queries and keys of qk_nope_head_dim + qk_rope_head_dim dims, the
+ * rotation on the qk_rope part): only the last rope_dim dims of every query
+ * and key row are rotated, pair j of that part by freqs_cis[p, j]
+ * (freqs_cis: device f32 [max_pos, rope_dim / 2, 2]); the first
+ * head_dim - rope_dim dims are copied unchanged; value rows (v_head_dim
+ * wide) are copied.  k_new is [n_new, n_kv_heads, head_dim], v_new
+ * [n_new, n_kv_heads, v_head_dim].  pkv_rope_kv_store is this call with
+ * rope_dim = head_dim.  Errors: as pkv_rope_kv_store, plus PKV_ERR_SHAPE
+ * when rope_dim is not in (0, head_dim] or not a multiple of 16 bytes of
+ * elements (8 for bf16, 4 for f32). */
+pkv_status pkv_rope_kv_store_partial(const pkv_pool *pool, int32_t layer_id, const void *q,
+                                     void *q_out, int32_t n_heads, const void *k_new,
+                                     const void *v_new, const int32_t *position_ids,
+                                     const float *freqs_cis, int64_t max_pos, int32_t rope_dim,
+                                     const int32_t *out_cache_loc, int64_t n_new, void *stream);
 
 /* ------------------------------------------------------------------------
  * One decode step in one launch ("Inference" guide, section "KVCache System":

@@ -78,14 +78,14 @@ def decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceSte
                 out=None, write_kv: bool = True):
     """K/V write of the step's new tokens, split decode, merge.  Returns out."""
     import torch
-    H, d = int(q.shape[1]), int(q.shape[2])
+    H, d = int(q.shape[1]), int(v_buffer.shape[3])   # outputs: value width
     if num_splits is None:
         num_splits = B.pkv_decode_pick_splits(step.batch, int(k_buffer.shape[2]), H,
                                               step.max_len, step.total_len)
     if workspace is None:
         workspace = decode_workspace(step.batch, H, d, num_splits, q.device)
     if out is None:
-        out = torch.empty_like(q)
+        out = q.new_empty((q.shape[0], q.shape[1], v_buffer.shape[3]))
     if write_kv:
         B.pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id, k_new, v_new,
                        step.out_cache_loc, page_size=step.page_size)
@@ -107,7 +107,7 @@ def fused_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: Dev
     """The decode step (K/V write, split attention, merge) in one library call:
     one launch for bf16 pools with head_dim 128.  Returns out."""
     import torch
-    H, d = int(q.shape[1]), int(q.shape[2])
+    H, d = int(q.shape[1]), int(v_buffer.shape[3])   # outputs: value width
     if num_splits is None:
         num_splits = B.pkv_decode_step_pick_splits(step.batch, int(k_buffer.shape[2]), H,
                                                    step.max_len, step.total_len)
@@ -116,7 +116,7 @@ def fused_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: Dev
     if sync is None:
         sync = decode_sync(step.batch, H, q.device)
     if out is None:
-        out = torch.empty_like(q)
+        out = q.new_empty((q.shape[0], q.shape[1], v_buffer.shape[3]))
     B.pkv_paged_decode_step(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, k_new, v_new,
                             sm_scale, num_splits, workspace, sync, out,
                             page_size=step.page_size)
@@ -130,14 +130,14 @@ def stored_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: De
     split kernel also writes the new token's K/V (bf16 pools with head_dim
     128).  Returns out."""
     import torch
-    H, d = int(q.shape[1]), int(q.shape[2])
+    H, d = int(q.shape[1]), int(v_buffer.shape[3])   # outputs: value width
     if num_splits is None:
         num_splits = B.pkv_decode_pick_splits(step.batch, int(k_buffer.shape[2]), H,
                                               step.max_len, step.total_len)
     if workspace is None:
         workspace = decode_workspace(step.batch, H, d, num_splits, q.device)
     if out is None:
-        out = torch.empty_like(q)
+        out = q.new_empty((q.shape[0], q.shape[1], v_buffer.shape[3]))
     B.pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, k_new, v_new,
                              sm_scale, num_splits, workspace, out, page_size=step.page_size)
     return out
@@ -178,14 +178,14 @@ def shared_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: De
     """The decode step with each prefix group's shared keys read once
     (pkv_paged_decode_shared).  Returns out."""
     import torch
-    H, d = int(q.shape[1]), int(q.shape[2])
+    H, d = int(q.shape[1]), int(v_buffer.shape[3])   # outputs: value width
     ns, ps = groups.pick_splits(step, int(k_buffer.shape[2]), H)
     num_splits = ns if num_splits is None else num_splits
     prefix_splits = ps if prefix_splits is None else prefix_splits
     if workspace is None:
         workspace = decode_workspace(step.batch, H, d, num_splits + prefix_splits, q.device)
     if out is None:
-        out = torch.empty_like(q)
+        out = q.new_empty((q.shape[0], q.shape[1], v_buffer.shape[3]))
     B.pkv_paged_decode_shared(k_buffer, v_buffer, req_to_token, layer_id, step.c, groups.c, q,
                               k_new, v_new, sm_scale, num_splits, prefix_splits, workspace, out,
                               page_size=step.page_size)
@@ -202,17 +202,19 @@ def advance_decode(k_buffer, v_buffer, req_to_token, step: DeviceStep) -> None:
 
 
 def rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q, k_new,
-                  v_new, freqs_cis, q_out=None):
+                  v_new, freqs_cis, q_out=None, rope_dim: Optional[int] = None):
     """Rotate the step's new queries and keys by their positions' rows of the
     rotary table freqs_cis [max_pos, head_dim / 2, 2] (f32 [cos, sin]) and
-    write the rotated keys and the values to the pool, in one launch.
-    Returns the rotated queries (q_out; pass q_out=q to rotate in place)."""
+    write the rotated keys and the values to the pool, in one launch.  With
+    rope_dim (MLA-shaped rows) only the last rope_dim dims turn and the table
+    is [max_pos, rope_dim / 2, 2].  Returns the rotated queries (q_out; pass
+    q_out=q to rotate in place)."""
     import torch
     if q_out is None:
         q_out = torch.empty_like(q)
     B.pkv_rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id, q, q_out, k_new, v_new,
                         step.position_ids, freqs_cis, step.out_cache_loc,
-                        page_size=step.page_size)
+                        page_size=step.page_size, rope_dim=rope_dim)
     return q_out
 
 
@@ -223,7 +225,7 @@ def prefill_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceSt
     step's launch schedule of non-empty row blocks unless schedule=False)."""
     import torch
     if out is None:
-        out = torch.empty_like(q)
+        out = q.new_empty((q.shape[0], q.shape[1], v_buffer.shape[3]))
     if write_kv:
         B.pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id, k_new, v_new,
                        step.out_cache_loc, page_size=step.page_size)

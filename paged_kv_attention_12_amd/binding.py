@@ -37,6 +37,7 @@ EXPORTED = (
     "pkv_paged_decode_step", "pkv_decode_step_pick_splits", "pkv_paged_decode_store",
     "pkv_build_positions", "pkv_rope_kv_store", "pkv_decode_advance", "pkv_prefill_blocks",
     "pkv_paged_decode_store_noalloc", "pkv_decode_prefix_groups", "pkv_paged_decode_shared",
+    "pkv_rope_kv_store_partial",
 )
 
 PKV_PREFIX_GROUP_MAX = 16
@@ -54,7 +55,7 @@ class pkv_pool(C.Structure):
         ("k_buffer", C.c_void_p), ("v_buffer", C.c_void_p), ("req_to_token", C.c_void_p),
         ("n_layers", C.c_int64), ("size", C.c_int64), ("num_reqs", C.c_int64),
         ("max_ctx_len", C.c_int64), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
-        ("dtype", C.c_int32), ("page_size", C.c_int32),
+        ("dtype", C.c_int32), ("page_size", C.c_int32), ("v_head_dim", C.c_int32),
     ]
 
 
@@ -126,6 +127,8 @@ def load() -> C.CDLL:
         "pkv_build_positions": (C.c_int, [i32, P, P, P, i64, C.POINTER(C.c_int64)]),
         "pkv_rope_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, i32, P, P, P, P, i64, P,
                                         i64, P]),
+        "pkv_rope_kv_store_partial": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, i32, P, P, P, P,
+                                                i64, i32, P, i64, P]),
         "pkv_decode_advance": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, P, P, P, P]),
         "pkv_prefill_blocks": (C.c_int, [i32, P, P, i32, i32, P, i64, C.POINTER(C.c_int64)]),
     }
@@ -194,14 +197,33 @@ def dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _check_q_out(q, out, k_buffer, v_buffer, rows: int) -> None:
+    """q [rows, n_heads, head_dim] and out [rows, n_heads, v_head_dim] in the pool dtype."""
+    if q.dim() != 3 or q.shape[0] != rows or q.shape[2] != k_buffer.shape[3] \
+            or q.dtype != k_buffer.dtype or out.dim() != 3 \
+            or tuple(out.shape) != (q.shape[0], q.shape[1], v_buffer.shape[3]) \
+            or out.dtype != q.dtype:
+        raise ValueError("q must be [rows, n_heads, head_dim] and out [rows, n_heads, "
+                         "v_head_dim] in the pool dtype")
+
+
+def _check_new(k_new, v_new, k_buffer, v_buffer, rows: int) -> None:
+    """k_new [rows, n_kv_heads, head_dim], v_new [rows, n_kv_heads, v_head_dim]."""
+    if tuple(k_new.shape) != (rows,) + tuple(k_buffer.shape[2:]) \
+            or tuple(v_new.shape) != (rows,) + tuple(v_buffer.shape[2:]) \
+            or k_new.dtype != k_buffer.dtype or v_new.dtype != k_buffer.dtype:
+        raise ValueError("k_new / v_new must be [rows, n_kv_heads, head_dim / v_head_dim] in "
+                         "the pool dtype")
+
+
 def make_pool(k_buffer, v_buffer, req_to_token, page_size: int = 1) -> pkv_pool:
     """pkv_pool view of device tensors k_buffer / v_buffer [n_layers, size,
     n_kv_heads, head_dim] and req_to_token int32 [num_reqs, entries]: slots
     (page_size 1, max_ctx_len = entries) or physical page ids of pages of
     page_size tokens (max_ctx_len = entries * page_size)."""
     import torch
-    if k_buffer.shape != v_buffer.shape or k_buffer.dtype != v_buffer.dtype:
-        raise ValueError("k_buffer and v_buffer differ in shape or dtype")
+    if k_buffer.shape[:3] != v_buffer.shape[:3] or k_buffer.dtype != v_buffer.dtype:
+        raise ValueError("k_buffer and v_buffer differ in layers, slots, heads or dtype")
     if k_buffer.dim() != 4 or req_to_token.dim() != 2:
         raise ValueError("pool must be 4-D and req_to_token 2-D")
     p = pkv_pool()
@@ -209,6 +231,7 @@ def make_pool(k_buffer, v_buffer, req_to_token, page_size: int = 1) -> pkv_pool:
     p.v_buffer = _dev_ptr(v_buffer, "v_buffer")
     p.req_to_token = _dev_ptr(req_to_token, "req_to_token", torch.int32)
     p.n_layers, p.size, p.n_kv_heads, p.head_dim = (int(s) for s in k_buffer.shape)
+    p.v_head_dim = int(v_buffer.shape[3])
     p.num_reqs = int(req_to_token.shape[0])
     p.max_ctx_len = int(req_to_token.shape[1]) * max(int(page_size), 1)
     p.page_size = int(page_size)
@@ -330,11 +353,8 @@ def pkv_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, k_new, v_new,
     import torch
     pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
     n_new = int(out_cache_loc.numel())
-    if n_new and (k_new.shape[0] != n_new or v_new.shape[0] != n_new
-                  or tuple(k_new.shape[1:]) != tuple(k_buffer.shape[2:])
-                  or k_new.shape != v_new.shape or k_new.dtype != k_buffer.dtype
-                  or v_new.dtype != k_buffer.dtype):
-        raise ValueError("k_new / v_new must be [n_new, n_kv_heads, head_dim] in the pool dtype")
+    if n_new:
+        _check_new(k_new, v_new, k_buffer, v_buffer, n_new)
     st = load().pkv_kv_store(C.byref(pool), int(layer_id),
                              _dev_ptr(k_new, "k_new") if n_new else 0,
                              _dev_ptr(v_new, "v_new") if n_new else 0,
@@ -389,13 +409,8 @@ def pkv_paged_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step:
                           out, page_size: int = 1) -> None:
     import torch
     pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
-    if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
-            or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("q / out must be [batch, n_heads, head_dim] in the pool dtype")
-    if tuple(k_new.shape) != (step.batch,) + tuple(k_buffer.shape[2:]) \
-            or k_new.shape != v_new.shape or k_new.dtype != k_buffer.dtype \
-            or v_new.dtype != k_buffer.dtype:
-        raise ValueError("k_new / v_new must be [batch, n_kv_heads, head_dim] in the pool dtype")
+    _check_q_out(q, out, k_buffer, v_buffer, step.batch)
+    _check_new(k_new, v_new, k_buffer, v_buffer, step.batch)
     st = load().pkv_paged_decode_step(
         C.byref(pool), int(layer_id), C.byref(step), _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"),
         _dev_ptr(v_new, "v_new"), int(q.shape[1]), float(sm_scale), int(num_splits),
@@ -408,13 +423,8 @@ def pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id: int, step
                            k_new, v_new, sm_scale: float, num_splits: int, workspace,
                            out, page_size: int = 1) -> None:
     pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
-    if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
-            or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("q / out must be [batch, n_heads, head_dim] in the pool dtype")
-    if tuple(k_new.shape) != (step.batch,) + tuple(k_buffer.shape[2:]) \
-            or k_new.shape != v_new.shape or k_new.dtype != k_buffer.dtype \
-            or v_new.dtype != k_buffer.dtype:
-        raise ValueError("k_new / v_new must be [batch, n_kv_heads, head_dim] in the pool dtype")
+    _check_q_out(q, out, k_buffer, v_buffer, step.batch)
+    _check_new(k_new, v_new, k_buffer, v_buffer, step.batch)
     st = load().pkv_paged_decode_store(
         C.byref(pool), int(layer_id), C.byref(step), _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"),
         _dev_ptr(v_new, "v_new"), int(q.shape[1]), float(sm_scale), int(num_splits),
@@ -429,13 +439,8 @@ def pkv_paged_decode_store_noalloc(k_buffer, v_buffer, req_to_token, layer_id: i
     """pkv_paged_decode_store with the split partials in the library's static
     per-device scratch array instead of a caller workspace."""
     pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
-    if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
-            or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("q / out must be [batch, n_heads, head_dim] in the pool dtype")
-    if tuple(k_new.shape) != (step.batch,) + tuple(k_buffer.shape[2:]) \
-            or k_new.shape != v_new.shape or k_new.dtype != k_buffer.dtype \
-            or v_new.dtype != k_buffer.dtype:
-        raise ValueError("k_new / v_new must be [batch, n_kv_heads, head_dim] in the pool dtype")
+    _check_q_out(q, out, k_buffer, v_buffer, step.batch)
+    _check_new(k_new, v_new, k_buffer, v_buffer, step.batch)
     st = load().pkv_paged_decode_store_noalloc(
         C.byref(pool), int(layer_id), C.byref(step), _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"),
         _dev_ptr(v_new, "v_new"), int(q.shape[1]), float(sm_scale), int(num_splits),
@@ -485,13 +490,8 @@ def pkv_paged_decode_shared(k_buffer, v_buffer, req_to_token, layer_id: int, ste
                             sm_scale: float, num_splits: int, prefix_splits: int, workspace,
                             out, page_size: int = 1) -> None:
     pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
-    if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
-            or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("q / out must be [batch, n_heads, head_dim] in the pool dtype")
-    if tuple(k_new.shape) != (step.batch,) + tuple(k_buffer.shape[2:]) \
-            or k_new.shape != v_new.shape or k_new.dtype != k_buffer.dtype \
-            or v_new.dtype != k_buffer.dtype:
-        raise ValueError("k_new / v_new must be [batch, n_kv_heads, head_dim] in the pool dtype")
+    _check_q_out(q, out, k_buffer, v_buffer, step.batch)
+    _check_new(k_new, v_new, k_buffer, v_buffer, step.batch)
     st = load().pkv_paged_decode_shared(
         C.byref(pool), int(layer_id), C.byref(step), C.byref(groups) if groups is not None else None,
         _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"), int(q.shape[1]),
@@ -501,28 +501,35 @@ def pkv_paged_decode_shared(k_buffer, v_buffer, req_to_token, layer_id: int, ste
 
 
 def pkv_rope_kv_store(k_buffer, v_buffer, req_to_token, layer_id: int, q, q_out, k_new, v_new,
-                      position_ids, freqs_cis, out_cache_loc, page_size: int = 1) -> None:
+                      position_ids, freqs_cis, out_cache_loc, page_size: int = 1,
+                      rope_dim: Optional[int] = None) -> None:
+    """Rotary write of the new tokens (pkv_rope_kv_store); with rope_dim, only
+    the last rope_dim dims of each query / key row turn
+    (pkv_rope_kv_store_partial, freqs_cis [max_pos, rope_dim / 2, 2])."""
     import torch
     pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
     n_new = int(k_new.shape[0])
     if q.dim() != 3 or q.shape[0] != n_new or q.shape[2] != k_buffer.shape[3] \
             or q.dtype != k_buffer.dtype or q_out.shape != q.shape or q_out.dtype != q.dtype:
         raise ValueError("q / q_out must be [n_new, n_heads, head_dim] in the pool dtype")
-    if tuple(k_new.shape[1:]) != tuple(k_buffer.shape[2:]) or k_new.shape != v_new.shape \
-            or k_new.dtype != k_buffer.dtype or v_new.dtype != k_buffer.dtype:
-        raise ValueError("k_new / v_new must be [n_new, n_kv_heads, head_dim] in the pool dtype")
-    if freqs_cis.dim() != 3 or freqs_cis.shape[1:] != (k_buffer.shape[3] // 2, 2) \
+    _check_new(k_new, v_new, k_buffer, v_buffer, n_new)
+    R = int(k_buffer.shape[3]) if rope_dim is None else int(rope_dim)
+    if freqs_cis.dim() != 3 or tuple(freqs_cis.shape[1:]) != (R // 2, 2) \
             or freqs_cis.dtype != torch.float32:
-        raise ValueError("freqs_cis must be float32 [max_pos, head_dim / 2, 2]")
+        raise ValueError("freqs_cis must be float32 [max_pos, rotated dims / 2, 2]")
     if position_ids.numel() != n_new or out_cache_loc.numel() != n_new:
         raise ValueError("position_ids / out_cache_loc must hold n_new entries")
-    st = load().pkv_rope_kv_store(
-        C.byref(pool), int(layer_id), _dev_ptr(q, "q"), _dev_ptr(q_out, "q_out"), int(q.shape[1]),
-        _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
-        _dev_ptr(position_ids, "position_ids", torch.int32),
-        _dev_ptr(freqs_cis, "freqs_cis", torch.float32), int(freqs_cis.shape[0]),
-        _dev_ptr(out_cache_loc, "out_cache_loc", torch.int32), n_new, _stream())
-    _check(st, "pkv_rope_kv_store")
+    args = [C.byref(pool), int(layer_id), _dev_ptr(q, "q"), _dev_ptr(q_out, "q_out"),
+            int(q.shape[1]), _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
+            _dev_ptr(position_ids, "position_ids", torch.int32),
+            _dev_ptr(freqs_cis, "freqs_cis", torch.float32), int(freqs_cis.shape[0])]
+    tail = [_dev_ptr(out_cache_loc, "out_cache_loc", torch.int32), n_new, _stream()]
+    if rope_dim is None:
+        st = load().pkv_rope_kv_store(*args, *tail)
+        _check(st, "pkv_rope_kv_store")
+    else:
+        st = load().pkv_rope_kv_store_partial(*args, R, *tail)
+        _check(st, "pkv_rope_kv_store_partial")
 
 
 def pkv_decode_advance(k_buffer, v_buffer, req_to_token, req_pool_indices, seq_lens, kv_indptr,
@@ -545,9 +552,7 @@ def pkv_decode_advance(k_buffer, v_buffer, req_to_token, req_pool_indices, seq_l
 def pkv_paged_prefill(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,
                       sm_scale: float, causal: bool, out, page_size: int = 1) -> None:
     pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
-    if q.dim() != 3 or q.shape[0] != step.n_new or q.shape[2] != k_buffer.shape[3] \
-            or q.dtype != k_buffer.dtype or out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("q / out must be [n_new, n_heads, head_dim] in the pool dtype")
+    _check_q_out(q, out, k_buffer, v_buffer, step.n_new)
     st = load().pkv_paged_prefill(C.byref(pool), int(layer_id), C.byref(step), _dev_ptr(q, "q"),
                                   int(q.shape[1]), float(sm_scale), 1 if causal else 0,
                                   _dev_ptr(out, "out"), _stream())

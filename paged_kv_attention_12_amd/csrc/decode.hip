@@ -399,7 +399,7 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, const 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-constexpr int kMfmaD = 128;  // head_dim of the matrix-core path
+constexpr int kMfmaD = 128;  // value width (and key width unless DK says otherwise)
 constexpr int kRing = 2;     // register tile sets of a wavefront (3 and 4 measured no faster)
 constexpr int kKT = 32;      // keys per iteration of a wavefront
 
@@ -418,13 +418,14 @@ constexpr int kKT = 32;      // keys per iteration of a wavefront
 // kSlotTile).  On return o[e][i] holds the
 // unnormalised O[column c][32g + 8i + e] against the base-2 running max m_run,
 // and l_tot the running sum (both per column, equal in the four lane groups).
-template <int TS, bool NEW, int P>
+template <int TS, bool NEW, int P, int DK = kMfmaD>
 __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot, int pool_row,
                                             int start, int end, int first, bool active, int hk,
                                             const uint16_t *qcol, const uint16_t *knew,
                                             const uint16_t *vnew, int newpos, f32x4_t (&o)[8],
                                             float &m_run, float &l_tot) {
-  constexpr int D = kMfmaD;
+  constexpr int D = kMfmaD;  // value width
+  constexpr int KS = DK / 32;  // 32-dim steps over the key width
   constexpr int KT = kKT;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
@@ -454,13 +455,14 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
   load_run(start);  // first on the dependent chain to the K/V rows
 
   // Q^T operand: column c, dims 8g + 32k .. +8 for step k.
-  uint4 qf[4];
+  uint4 qf[KS];
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+  for (int k = 0; k < KS; ++k)
     qf[k] = (active && qcol) ? load16(qcol + 8 * g + 32 * k) : make_uint4(0u, 0u, 0u, 0u);
 
-  const int64_t row_elems = (int64_t)a.n_kv_heads * D;
-  const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k_layer) + (int64_t)hk * D + 8 * g;
+  const int64_t krow_elems = (int64_t)a.n_kv_heads * DK;
+  const int64_t vrow_elems = (int64_t)a.n_kv_heads * D;
+  const uint16_t *kbase = reinterpret_cast<const uint16_t *>(a.k_layer) + (int64_t)hk * DK + 8 * g;
   const uint16_t *vbase = reinterpret_cast<const uint16_t *>(a.v_layer) + (int64_t)hk * D + 8 * c;
   const uint16_t *knew_l = NEW ? knew + 8 * g : nullptr;
   const uint16_t *vnew_l = NEW ? vnew + 8 * c : nullptr;
@@ -475,7 +477,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
   // of the round read the round's last row instead (finite data whose score is
   // masked to -inf, so its weight is 0): the loads stay unconditional, which
   // lets the compiler keep several tiles in flight.
-  auto fetch = [&](uint4(&kx)[2][4], uint4(&vx)[8], int j0, int r0, int r1) {
+  auto fetch = [&](uint4(&kx)[2][KS], uint4(&vx)[8], int j0, int r0, int r1) {
     const int last = r1 - 1 - r0;
     const int jb = j0 - r0;
     int jk[2], jv[8];
@@ -485,26 +487,26 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
     for (int x = 0; x < 8; ++x) jv[x] = min(jb + 16 * (x >> 2) + 4 * g + (x & 3), last);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint16_t *kp = kbase + (int64_t)s_slot[jk[t]] * row_elems;
+      const uint16_t *kp = kbase + (int64_t)s_slot[jk[t]] * krow_elems;
       if constexpr (NEW) kp = (r0 + jk[t] == newpos) ? knew_l : kp;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) kx[t][k] = load16(kp + 32 * k);
+      for (int k = 0; k < KS; ++k) kx[t][k] = load16(kp + 32 * k);
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      const uint16_t *vp = vbase + (int64_t)s_slot[jv[x]] * row_elems;
+      const uint16_t *vp = vbase + (int64_t)s_slot[jv[x]] * vrow_elems;
       if constexpr (NEW) vp = (r0 + jv[x] == newpos) ? vnew_l : vp;
       vx[x] = load16(vp);
     }
   };
 
-  auto process = [&](const uint4(&kx)[2][4], const uint4(&vx)[8], int j0, int r1) {
+  auto process = [&](const uint4(&kx)[2][KS], const uint4(&vx)[8], int j0, int r1) {
     f32x4_t st[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) st[t] = mfma16(kx[t][k], qf[k], st[t]);
+      for (int k = 0; k < KS; ++k) st[t] = mfma16(kx[t][k], qf[k], st[t]);
     }
     float mx = kNegInf;
 #pragma unroll
@@ -559,7 +561,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
 
   // Ring of P register tile sets: P - 1 tiles are in flight while one is used.
   static_assert(P >= 2, "pipeline depth");
-  uint4 kr[P][2][4], vr[P][8];
+  uint4 kr[P][2][KS], vr[P][8];
   // Rounds of run_cap keys: a split of up to one chunk takes one round (or
   // rounds of kSlotTile), the last split's tail past num_splits * chunk more.
   for (int r0 = start; r0 < end; r0 += run_cap) {
@@ -597,10 +599,10 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
 // and the wavefront of head chunk 0 of each kv-head in the split holding that
 // position writes them to the pool slot out_cache_loc[b] (no wavefront of
 // the launch reads that pool row).
-template <bool NEW>
+template <bool NEW, int DK = kMfmaD>
 __device__ __forceinline__ void split_mfma_body(const StepArgs &sa, int32_t *s_slot, int b, int s,
                                                 int wx) {
-  constexpr int D = kMfmaD;
+  constexpr int D = kMfmaD;  // value width; keys are DK wide
   const DecodeArgs &a = sa.d;
 
   const int L = a.seq_lens[b];
@@ -630,15 +632,21 @@ __device__ __forceinline__ void split_mfma_body(const StepArgs &sa, int32_t *s_s
   uint4 new_piece = make_uint4(0u, 0u, 0u, 0u);
   uint16_t *new_dst = nullptr;
   if constexpr (NEW) {
-    const int64_t new_row = ((int64_t)b * a.n_kv_heads + hk) * D;  // element offset in k_new / v_new
-    knew = reinterpret_cast<const uint16_t *>(sa.k_new) + new_row;
-    vnew = reinterpret_cast<const uint16_t *>(sa.v_new) + new_row;
-    writer = active && g0 == 0 && start <= newpos && newpos < end && lane < 2 * D / 8;
+    const int64_t row = (int64_t)b * a.n_kv_heads + hk;  // row of k_new / v_new
+    knew = reinterpret_cast<const uint16_t *>(sa.k_new) + row * DK;
+    vnew = reinterpret_cast<const uint16_t *>(sa.v_new) + row * D;
+    // lanes [0, DK/8) carry the key row's 16-byte pieces, the next D/8 lanes
+    // the value row's
+    writer = active && g0 == 0 && start <= newpos && newpos < end && lane < (DK + D) / 8;
     if (writer) {
       const int64_t loc = sa.out_cache_loc[b];
-      const int64_t dst = (loc * a.n_kv_heads + hk) * D + 8 * (lane & 15);
-      new_piece = load16((lane < D / 8 ? knew : vnew) + 8 * (lane & 15));
-      new_dst = reinterpret_cast<uint16_t *>(lane < D / 8 ? sa.k_layer_w : sa.v_layer_w) + dst;
+      const bool is_k = lane < DK / 8;
+      const int piece = is_k ? lane : lane - DK / 8;
+      new_piece = load16((is_k ? knew : vnew) + 8 * piece);
+      new_dst = is_k ? reinterpret_cast<uint16_t *>(sa.k_layer_w) +
+                           (loc * a.n_kv_heads + hk) * DK + 8 * piece
+                     : reinterpret_cast<uint16_t *>(sa.v_layer_w) +
+                           (loc * a.n_kv_heads + hk) * D + 8 * piece;
     }
   }
 
@@ -672,14 +680,14 @@ __device__ __forceinline__ void split_mfma_body(const StepArgs &sa, int32_t *s_s
   // Only the split holding the new token substitutes its rows in the fetch;
   // every other split runs the plain loop.
   const uint16_t *qcol =
-      col_ok ? reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)b * a.n_heads + h0 + c) * D
+      col_ok ? reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)b * a.n_heads + h0 + c) * DK
              : nullptr;
   if (NEW && start <= newpos && newpos < end)
-    attend_mfma<1, true, kRing>(a, s_slot, pool_row, start, end, 0, active, hk, qcol, knew, vnew,
-                                newpos, o, m_run, l_tot);
+    attend_mfma<1, true, kRing, DK>(a, s_slot, pool_row, start, end, 0, active, hk, qcol, knew,
+                                    vnew, newpos, o, m_run, l_tot);
   else
-    attend_mfma<1, false, kRing>(a, s_slot, pool_row, start, end, 0, active, hk, qcol, nullptr,
-                                 nullptr, -1, o, m_run, l_tot);
+    attend_mfma<1, false, kRing, DK>(a, s_slot, pool_row, start, end, 0, active, hk, qcol,
+                                     nullptr, nullptr, -1, o, m_run, l_tot);
   if (NEW && writer) store16(new_dst, new_piece);
   if (!active || !col_ok) return;
   // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
@@ -696,10 +704,12 @@ __device__ __forceinline__ void split_mfma_body(const StepArgs &sa, int32_t *s_s
   }
 }
 
-template <bool NEW>
-__global__ void __launch_bounds__(256, 2) decode_split_mfma_kernel(const StepArgs sa) {
+// Keys 192 wide (MLA-shaped layers) hold more registers per wavefront: one
+// wavefront per SIMD, instead of two for 128-wide keys.
+template <bool NEW, int DK>
+__global__ void __launch_bounds__(256, DK == 128 ? 2 : 1) decode_split_mfma_kernel(const StepArgs sa) {
   __shared__ int32_t s_slot[kSlotTile];
-  split_mfma_body<NEW>(sa, s_slot, blockIdx.z, blockIdx.y, blockIdx.x);
+  split_mfma_body<NEW, DK>(sa, s_slot, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1030,12 +1040,17 @@ hipError_t decode_dispatch_ng(const DecodeArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_paged_decode(const DecodeArgs &args, int dtype, int head_dim,
+bool decode_mfma_shape(int dtype, int head_dim, int v_head_dim) {
+  return dtype == 1 && v_head_dim == kMfmaD && (head_dim == 128 || head_dim == 192);
+}
+
+hipError_t launch_paged_decode(const DecodeArgs &args, int dtype, int head_dim, int v_head_dim,
                                hipStream_t stream) {
   DecodeArgs a = args;
   // Query heads of a kv-head's group served by one wavefront: up to 16 on the
-  // matrix-core path (bf16, head_dim 128), up to 8 on the vector path.
-  const bool mfma = dtype == 1 && head_dim == 128;
+  // matrix-core path (bf16, values 128 wide, keys 128 or 192), up to 8 on the
+  // vector path.
+  const bool mfma = decode_mfma_shape(dtype, head_dim, v_head_dim);
   const int per_wave = mfma ? 16 : 8;
   a.n_chunks = (a.group + per_wave - 1) / per_wave;
   a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
@@ -1043,9 +1058,13 @@ hipError_t launch_paged_decode(const DecodeArgs &args, int dtype, int head_dim,
     StepArgs sa{};
     sa.d = a;
     const dim3 grid((a.n_kv_heads * a.n_chunks + 3) / 4, a.num_splits, a.batch);
-    hipLaunchKernelGGL(decode_split_mfma_kernel<false>, grid, dim3(256), 0, stream, sa);
+    if (head_dim == 192)
+      hipLaunchKernelGGL((decode_split_mfma_kernel<false, 192>), grid, dim3(256), 0, stream, sa);
+    else
+      hipLaunchKernelGGL((decode_split_mfma_kernel<false, 128>), grid, dim3(256), 0, stream, sa);
     return hipGetLastError();
   }
+  if (head_dim != v_head_dim) return hipErrorInvalidValue;
   if (dtype == 1) {
     if (head_dim == 128) return decode_dispatch_ng<uint16_t, 128>(a, stream);
     if (head_dim == 64) return decode_dispatch_ng<uint16_t, 64>(a, stream);
@@ -1067,13 +1086,16 @@ hipError_t launch_decode_step(const StepArgs &args, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_split_store(const StepArgs &args, hipStream_t stream) {
+hipError_t launch_decode_split_store(const StepArgs &args, int head_dim, hipStream_t stream) {
   StepArgs sa = args;
   DecodeArgs &a = sa.d;
   a.n_chunks = (a.group + 15) / 16;
   a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
   const dim3 grid((a.n_kv_heads * a.n_chunks + 3) / 4, a.num_splits, a.batch);
-  hipLaunchKernelGGL(decode_split_mfma_kernel<true>, grid, dim3(256), 0, stream, sa);
+  if (head_dim == 192)
+    hipLaunchKernelGGL((decode_split_mfma_kernel<true, 192>), grid, dim3(256), 0, stream, sa);
+  else
+    hipLaunchKernelGGL((decode_split_mfma_kernel<true, 128>), grid, dim3(256), 0, stream, sa);
   return hipGetLastError();
 }
 

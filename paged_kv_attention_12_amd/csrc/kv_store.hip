@@ -8,23 +8,25 @@
 
 namespace pkv {
 
-// One thread moves one W-byte piece of a K row and the same piece of the V
-// row.  Consecutive threads cover consecutive pieces of a row, so each row is
-// read and written as one contiguous, fully coalesced run.
+// One thread moves one W-byte piece of a K row and, where the value row is
+// that wide (values may be narrower than keys), the same piece of the V row.
+// Consecutive threads cover consecutive pieces of a row, so each row is read
+// and written as one contiguous, fully coalesced run.
 template <typename W>
 __global__ void __launch_bounds__(256) kv_store_kernel(KvStoreArgs a, int64_t total_pieces,
-                                                       int32_t pieces_per_row) {
+                                                       int32_t pieces_per_row,
+                                                       int32_t v_pieces_per_row) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= total_pieces) return;
   const int64_t i = t / pieces_per_row;
   const int32_t c = (int32_t)(t - i * pieces_per_row);
   const int64_t loc = a.out_cache_loc[i];
-  const int64_t src = i * pieces_per_row + c;
-  const int64_t dst = loc * pieces_per_row + c;
-  const W kx = reinterpret_cast<const W *>(a.k_new)[src];
-  const W vx = reinterpret_cast<const W *>(a.v_new)[src];
-  reinterpret_cast<W *>(a.k_layer)[dst] = kx;
-  reinterpret_cast<W *>(a.v_layer)[dst] = vx;
+  const W kx = reinterpret_cast<const W *>(a.k_new)[i * pieces_per_row + c];
+  reinterpret_cast<W *>(a.k_layer)[loc * pieces_per_row + c] = kx;
+  if (c < v_pieces_per_row) {
+    const W vx = reinterpret_cast<const W *>(a.v_new)[i * v_pieces_per_row + c];
+    reinterpret_cast<W *>(a.v_layer)[loc * v_pieces_per_row + c] = vx;
+  }
 }
 
 hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t stream) {
@@ -33,15 +35,17 @@ hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t stream) {
   auto go = [&](auto tag, int width) {
     using W = decltype(tag);
     const int32_t ppr = a.row_bytes / width;
+    const int32_t vppr = a.v_row_bytes / width;
     const int64_t total = a.n_new * ppr;
     const int64_t blocks = (total + threads - 1) / threads;
     hipLaunchKernelGGL(kv_store_kernel<W>, dim3((uint32_t)blocks), dim3(threads), 0, stream, a,
-                       total, ppr);
+                       total, ppr, vppr);
     return hipGetLastError();
   };
-  if (a.row_bytes % 16 == 0) return go(uint4{}, 16);
-  if (a.row_bytes % 8 == 0) return go(uint2{}, 8);
-  if (a.row_bytes % 4 == 0) return go(uint32_t{}, 4);
+  const int32_t both = a.row_bytes | a.v_row_bytes;
+  if (both % 16 == 0) return go(uint4{}, 16);
+  if (both % 8 == 0) return go(uint2{}, 8);
+  if (both % 4 == 0) return go(uint32_t{}, 4);
   return go(uint16_t{}, 2);
 }
 

@@ -19,7 +19,8 @@ struct KvStoreArgs {
   const int32_t *out_cache_loc;
   int64_t n_new;
   int64_t size;
-  int32_t row_bytes;          // n_kv_heads * head_dim * sizeof(dtype)
+  int32_t row_bytes;          // key row: n_kv_heads * head_dim * sizeof(dtype)
+  int32_t v_row_bytes;        // value row: n_kv_heads * v_head_dim * sizeof(dtype) (<= row_bytes)
 };
 hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t stream);
 
@@ -68,8 +69,12 @@ struct DecodeArgs {
   // which splits hold keys); 0: every split writes one.
   int32_t skip_empty;
 };
-// dtype: 0 = f32, 1 = bf16
-hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, hipStream_t stream);
+// dtype: 0 = f32, 1 = bf16.  head_dim: key width; v_head_dim: value width.
+hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, int v_head_dim,
+                               hipStream_t stream);
+// Shapes the matrix-core split kernel takes: bf16, values 128 wide, keys 128
+// or 192 wide (the split-with-write and shared-prefix paths need them).
+bool decode_mfma_shape(int dtype, int head_dim, int v_head_dim);
 
 // One fused decode step (bf16, head_dim 128): new-token K/V write, split
 // attention and merge in one launch.
@@ -88,7 +93,7 @@ hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream);
 // The split attention of one decode step with the new-token K/V write folded
 // in (bf16, head_dim 128); sync, out and tasks are not used.  The merge is a
 // separate launch.
-hipError_t launch_decode_split_store(const StepArgs &a, hipStream_t stream);
+hipError_t launch_decode_split_store(const StepArgs &a, int head_dim, hipStream_t stream);
 
 // Rotary embedding of the new tokens fused with their K/V write.
 struct RopeArgs {
@@ -105,7 +110,9 @@ struct RopeArgs {
   int64_t n_new;
   int32_t n_heads;
   int32_t n_kv_heads;
-  int32_t head_dim;
+  int32_t head_dim;           // query / key rows
+  int32_t v_head_dim;         // value rows
+  int32_t rope_dim;           // rotated part: the last rope_dim dims of each row
 };
 // dtype: 0 = f32, 1 = bf16
 hipError_t launch_rope_kv_store(const RopeArgs &a, int dtype, hipStream_t stream);
@@ -185,7 +192,9 @@ struct PrefillArgs {
   int32_t causal;
   float scale_log2;
 };
-hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, hipStream_t stream);
+// head_dim: query / key width; v_head_dim: value / output width.
+hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, int v_head_dim,
+                                hipStream_t stream);
 constexpr int kPrefillBlockRows = 256;  // query rows of one prefill workgroup
 
 }  // namespace pkv

@@ -42,11 +42,21 @@ int64_t table_stride_of(int64_t max_ctx_len, int page_shift) {
   return (max_ctx_len + (int64_t(1) << page_shift) - 1) >> page_shift;
 }
 
+// Width of the value rows (0 in the pool: as wide as the keys).
+int32_t v_dim(const pkv_pool *p) { return p->v_head_dim > 0 ? p->v_head_dim : p->head_dim; }
+
+// Key / value widths the attention kernels take: equal widths of 64 or 128,
+// or MLA-shaped keys of 192 with values of 128.
+bool dims_ok(const pkv_pool *p) {
+  const int32_t dk = p->head_dim, dv = v_dim(p);
+  return (dk == dv && (dk == 64 || dk == 128)) || (dk == 192 && dv == 128);
+}
+
 pkv_status check_pool(const pkv_pool *p, int32_t layer_id) {
   if (!p || !p->k_buffer || !p->v_buffer || !p->req_to_token) return PKV_ERR_NULL;
   if (!dtype_ok(p->dtype)) return PKV_ERR_DTYPE;
   if (p->n_layers <= 0 || p->size <= 0 || p->num_reqs <= 0 || p->max_ctx_len <= 0 ||
-      p->n_kv_heads <= 0 || p->head_dim <= 0)
+      p->n_kv_heads <= 0 || p->head_dim <= 0 || p->v_head_dim < 0 || v_dim(p) > p->head_dim)
     return PKV_ERR_SHAPE;
   if (p->size > INT32_MAX) return PKV_ERR_SHAPE;  // slots are int32
   if (p->max_ctx_len > INT32_MAX) return PKV_ERR_SHAPE;  // positions are int32
@@ -65,9 +75,16 @@ void set_table(Args &a, const pkv_pool *p) {
   a.table_stride = table_stride_of(p->max_ctx_len, a.page_shift);
 }
 
-const char *layer_ptr(const void *buf, const pkv_pool *p, int32_t layer_id) {
-  const int64_t row = (int64_t)p->n_kv_heads * p->head_dim * (int64_t)dtype_bytes(p->dtype);
+// First byte of layer layer_id of a pool buffer whose rows are `dim` wide.
+const char *layer_ptr(const void *buf, const pkv_pool *p, int32_t layer_id, int32_t dim) {
+  const int64_t row = (int64_t)p->n_kv_heads * dim * (int64_t)dtype_bytes(p->dtype);
   return reinterpret_cast<const char *>(buf) + (int64_t)layer_id * p->size * row;
+}
+const char *k_layer_ptr(const pkv_pool *p, int32_t layer_id) {
+  return layer_ptr(p->k_buffer, p, layer_id, p->head_dim);
+}
+const char *v_layer_ptr(const pkv_pool *p, int32_t layer_id) {
+  return layer_ptr(p->v_buffer, p, layer_id, v_dim(p));
 }
 
 // Merge of split partials that skip_empty split kernels wrote: only the
@@ -282,16 +299,18 @@ pkv_status pkv_kv_store(const pkv_pool *pool, int32_t layer_id, const void *k_ne
   if (n_new == 0) return PKV_OK;
   if (!k_new || !v_new || !out_cache_loc) return PKV_ERR_NULL;
   const int64_t row_bytes = (int64_t)pool->n_kv_heads * pool->head_dim * dtype_bytes(pool->dtype);
+  const int64_t v_row_bytes = (int64_t)pool->n_kv_heads * v_dim(pool) * dtype_bytes(pool->dtype);
   if (row_bytes > INT32_MAX) return PKV_ERR_SHAPE;
   pkv::KvStoreArgs a{};
-  a.k_layer = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
-  a.v_layer = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
+  a.k_layer = const_cast<char *>(k_layer_ptr(pool, layer_id));
+  a.v_layer = const_cast<char *>(v_layer_ptr(pool, layer_id));
   a.k_new = k_new;
   a.v_new = v_new;
   a.out_cache_loc = out_cache_loc;
   a.n_new = n_new;
   a.size = pool->size;
   a.row_bytes = (int32_t)row_bytes;
+  a.v_row_bytes = (int32_t)v_row_bytes;
   return hip_status(pkv::launch_kv_store(a, (hipStream_t)stream));
 }
 
@@ -336,23 +355,25 @@ pkv_status pkv_paged_decode(const pkv_pool *pool, int32_t layer_id, const pkv_st
   if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || num_splits <= 0 ||
       num_splits > 65535 || step->batch > 65535)
     return PKV_ERR_SHAPE;
-  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!dims_ok(pool)) return PKV_ERR_UNSUPPORTED;
+  // unequal key / value widths run on the bf16 matrix-core kernel only
+  if (pool->head_dim != v_dim(pool) && pool->dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale)) return PKV_ERR_SHAPE;
   if (step->batch == 0) return PKV_OK;
   if (!step->req_pool_indices || !step->seq_lens) return PKV_ERR_NULL;
   if (step->max_len <= 0 || step->max_len > pool->max_ctx_len) return PKV_ERR_SHAPE;
-  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, pool->head_dim, num_splits))
+  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, v_dim(pool), num_splits))
     return PKV_ERR_WORKSPACE_TOO_SMALL;
   const int32_t group = n_heads / pool->n_kv_heads;
   pkv::DecodeArgs a{};
-  a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
-  a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
+  a.k_layer = k_layer_ptr(pool, layer_id);
+  a.v_layer = v_layer_ptr(pool, layer_id);
   set_table(a, pool);
   a.req_pool_indices = step->req_pool_indices;
   a.seq_lens = step->seq_lens;
   a.q = q;
   a.o_part = reinterpret_cast<float *>(workspace);
-  a.ml_part = a.o_part + (size_t)step->batch * n_heads * num_splits * pool->head_dim;
+  a.ml_part = a.o_part + (size_t)step->batch * n_heads * num_splits * v_dim(pool);
   a.batch = step->batch;
   a.n_heads = n_heads;
   a.n_kv_heads = pool->n_kv_heads;
@@ -366,7 +387,7 @@ pkv_status pkv_paged_decode(const pkv_pool *pool, int32_t layer_id, const pkv_st
   a.skip_empty = 0;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   return hip_status(pkv::launch_paged_decode(a, pool->dtype == PKV_BF16 ? 1 : 0,
-                                              pool->head_dim, (hipStream_t)stream));
+                                              pool->head_dim, v_dim(pool), (hipStream_t)stream));
 }
 
 int32_t pkv_decode_step_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_heads,
@@ -388,7 +409,7 @@ pkv_status pkv_paged_decode_step(const pkv_pool *pool, int32_t layer_id, const p
   if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || num_splits <= 0 ||
       num_splits > 65535 || step->batch > 65535)
     return PKV_ERR_SHAPE;
-  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!dims_ok(pool)) return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale)) return PKV_ERR_SHAPE;
   if (step->batch == 0) return PKV_OK;
   if (!k_new || !v_new || !step->out_cache_loc || !step->req_pool_indices || !step->seq_lens)
@@ -396,28 +417,28 @@ pkv_status pkv_paged_decode_step(const pkv_pool *pool, int32_t layer_id, const p
   if (step->n_new != step->batch) return PKV_ERR_SHAPE;  // one new token per request
   if (step->max_len <= 0 || step->max_len > pool->max_ctx_len) return PKV_ERR_SHAPE;
   if (sync_len < (int64_t)step->batch * n_heads) return PKV_ERR_SHAPE;
-  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, pool->head_dim, num_splits))
+  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, v_dim(pool), num_splits))
     return PKV_ERR_WORKSPACE_TOO_SMALL;
-  if (pool->dtype != PKV_BF16 || pool->head_dim != 128) {
+  if (pool->dtype != PKV_BF16 || pool->head_dim != 128 || v_dim(pool) != 128) {
     // No fused kernel for this shape: the same step as three launches.
     st = pkv_kv_store(pool, layer_id, k_new, v_new, step->out_cache_loc, step->n_new, stream);
     if (st != PKV_OK) return st;
     st = pkv_paged_decode(pool, layer_id, step, q, n_heads, sm_scale, num_splits, workspace,
                           ws_bytes, stream);
     if (st != PKV_OK) return st;
-    return pkv_paged_decode_merge(step->batch, n_heads, pool->head_dim, pool->dtype, num_splits,
+    return pkv_paged_decode_merge(step->batch, n_heads, v_dim(pool), pool->dtype, num_splits,
                                   workspace, ws_bytes, out, stream);
   }
   pkv::StepArgs sa{};
   pkv::DecodeArgs &a = sa.d;
-  a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
-  a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
+  a.k_layer = k_layer_ptr(pool, layer_id);
+  a.v_layer = v_layer_ptr(pool, layer_id);
   set_table(a, pool);
   a.req_pool_indices = step->req_pool_indices;
   a.seq_lens = step->seq_lens;
   a.q = q;
   a.o_part = reinterpret_cast<float *>(workspace);
-  a.ml_part = a.o_part + (size_t)step->batch * n_heads * num_splits * pool->head_dim;
+  a.ml_part = a.o_part + (size_t)step->batch * n_heads * num_splits * v_dim(pool);
   a.batch = step->batch;
   a.n_heads = n_heads;
   a.n_kv_heads = pool->n_kv_heads;
@@ -432,8 +453,8 @@ pkv_status pkv_paged_decode_step(const pkv_pool *pool, int32_t layer_id, const p
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   sa.k_new = k_new;
   sa.v_new = v_new;
-  sa.k_layer_w = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
-  sa.v_layer_w = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
+  sa.k_layer_w = const_cast<char *>(k_layer_ptr(pool, layer_id));
+  sa.v_layer_w = const_cast<char *>(v_layer_ptr(pool, layer_id));
   sa.out_cache_loc = step->out_cache_loc;
   sa.sync = sync;
   sa.out = out;
@@ -451,16 +472,16 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
   if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || num_splits <= 0 ||
       num_splits > 65535 || step->batch > 65535)
     return PKV_ERR_SHAPE;
-  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!dims_ok(pool)) return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(sm_scale)) return PKV_ERR_SHAPE;
   if (step->batch == 0) return PKV_OK;
   if (!k_new || !v_new || !step->out_cache_loc || !step->req_pool_indices || !step->seq_lens)
     return PKV_ERR_NULL;
   if (step->n_new != step->batch) return PKV_ERR_SHAPE;  // one new token per request
   if (step->max_len <= 0 || step->max_len > pool->max_ctx_len) return PKV_ERR_SHAPE;
-  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, pool->head_dim, num_splits))
+  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, v_dim(pool), num_splits))
     return PKV_ERR_WORKSPACE_TOO_SMALL;
-  if (pool->dtype != PKV_BF16 || pool->head_dim != 128) {
+  if (!pkv::decode_mfma_shape(pool->dtype == PKV_BF16 ? 1 : 0, pool->head_dim, v_dim(pool))) {
     st = pkv_kv_store(pool, layer_id, k_new, v_new, step->out_cache_loc, step->n_new, stream);
     if (st != PKV_OK) return st;
     st = pkv_paged_decode(pool, layer_id, step, q, n_heads, sm_scale, num_splits, workspace,
@@ -469,14 +490,14 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
   } else {
     pkv::StepArgs sa{};
     pkv::DecodeArgs &a = sa.d;
-    a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
-    a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
+    a.k_layer = k_layer_ptr(pool, layer_id);
+    a.v_layer = v_layer_ptr(pool, layer_id);
     set_table(a, pool);
     a.req_pool_indices = step->req_pool_indices;
     a.seq_lens = step->seq_lens;
     a.q = q;
     a.o_part = reinterpret_cast<float *>(workspace);
-    a.ml_part = a.o_part + (size_t)step->batch * n_heads * num_splits * pool->head_dim;
+    a.ml_part = a.o_part + (size_t)step->batch * n_heads * num_splits * v_dim(pool);
     a.batch = step->batch;
     a.n_heads = n_heads;
     a.n_kv_heads = pool->n_kv_heads;
@@ -488,18 +509,18 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     sa.k_new = k_new;
     sa.v_new = v_new;
-    sa.k_layer_w = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
-    sa.v_layer_w = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
+    sa.k_layer_w = const_cast<char *>(k_layer_ptr(pool, layer_id));
+    sa.v_layer_w = const_cast<char *>(v_layer_ptr(pool, layer_id));
     sa.out_cache_loc = step->out_cache_loc;
     // Splits past a request's keys leave no partial; the merge reads only the
     // ones that hold keys.
     a.skip_empty = 1;
-    st = hip_status(pkv::launch_decode_split_store(sa, (hipStream_t)stream));
+    st = hip_status(pkv::launch_decode_split_store(sa, pool->head_dim, (hipStream_t)stream));
     if (st != PKV_OK) return st;
     pkv::MergeArgs m = merge_args(a, out, nullptr, 0, 0);
-    return hip_status(pkv::launch_decode_merge(m, 1, pool->head_dim, (hipStream_t)stream));
+    return hip_status(pkv::launch_decode_merge(m, 1, v_dim(pool), (hipStream_t)stream));
   }
-  return pkv_paged_decode_merge(step->batch, n_heads, pool->head_dim, pool->dtype, num_splits,
+  return pkv_paged_decode_merge(step->batch, n_heads, v_dim(pool), pool->dtype, num_splits,
                                 workspace, ws_bytes, out, stream);
 }
 
@@ -630,7 +651,7 @@ pkv_status pkv_paged_decode_shared(const pkv_pool *pool, int32_t layer_id, const
   if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || num_splits <= 0 ||
       num_splits > 65535 || step->batch > 65535)
     return PKV_ERR_SHAPE;
-  const bool mfma = pool->dtype == PKV_BF16 && pool->head_dim == 128;
+  const bool mfma = pool->dtype == PKV_BF16 && pool->head_dim == 128 && v_dim(pool) == 128;
   if (!pg || pg->n_groups <= 0 || !mfma)  // nothing shared, or no matrix-core path: plain step
     return pkv_paged_decode_store(pool, layer_id, step, q, k_new, v_new, n_heads, sm_scale,
                                   num_splits, workspace, ws_bytes, out, stream);
@@ -646,17 +667,17 @@ pkv_status pkv_paged_decode_shared(const pkv_pool *pool, int32_t layer_id, const
       pg->max_suffix > pool->max_ctx_len || (int64_t)num_splits + prefix_splits > 65535)
     return PKV_ERR_SHAPE;
   const int32_t total = num_splits + prefix_splits;
-  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, pool->head_dim, total))
+  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, v_dim(pool), total))
     return PKV_ERR_WORKSPACE_TOO_SMALL;
   pkv::DecodeArgs a{};
-  a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
-  a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
+  a.k_layer = k_layer_ptr(pool, layer_id);
+  a.v_layer = v_layer_ptr(pool, layer_id);
   set_table(a, pool);
   a.req_pool_indices = step->req_pool_indices;
   a.seq_lens = step->seq_lens;
   a.q = q;
   a.o_part = reinterpret_cast<float *>(workspace);
-  a.ml_part = a.o_part + (size_t)step->batch * n_heads * total * pool->head_dim;
+  a.ml_part = a.o_part + (size_t)step->batch * n_heads * total * v_dim(pool);
   a.batch = step->batch;
   a.n_heads = n_heads;
   a.n_kv_heads = pool->n_kv_heads;
@@ -681,13 +702,13 @@ pkv_status pkv_paged_decode_shared(const pkv_pool *pool, int32_t layer_id, const
   sh.sfx.d.kv_start = pg->kv_start;
   sh.sfx.k_new = k_new;
   sh.sfx.v_new = v_new;
-  sh.sfx.k_layer_w = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
-  sh.sfx.v_layer_w = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
+  sh.sfx.k_layer_w = const_cast<char *>(k_layer_ptr(pool, layer_id));
+  sh.sfx.v_layer_w = const_cast<char *>(v_layer_ptr(pool, layer_id));
   sh.sfx.out_cache_loc = step->out_cache_loc;
   st = hip_status(pkv::launch_decode_shared(sh, (hipStream_t)stream));
   if (st != PKV_OK) return st;
   pkv::MergeArgs m = merge_args(sh.sfx.d, out, pg->kv_start, prefix_splits, sh.pfx.d.chunk);
-  return hip_status(pkv::launch_decode_merge(m, 1, pool->head_dim, (hipStream_t)stream));
+  return hip_status(pkv::launch_decode_merge(m, 1, v_dim(pool), (hipStream_t)stream));
 }
 
 pkv_status pkv_decode_advance(const pkv_pool *pool, int32_t batch, const int32_t *req_pool_indices,
@@ -709,16 +730,23 @@ pkv_status pkv_decode_advance(const pkv_pool *pool, int32_t batch, const int32_t
   return hip_status(pkv::launch_decode_advance(a, (hipStream_t)stream));
 }
 
-pkv_status pkv_rope_kv_store(const pkv_pool *pool, int32_t layer_id, const void *q, void *q_out,
-                             int32_t n_heads, const void *k_new, const void *v_new,
-                             const int32_t *position_ids, const float *freqs_cis,
-                             int64_t max_pos, const int32_t *out_cache_loc, int64_t n_new,
-                             void *stream) {
+}  // extern "C"
+
+namespace {
+
+pkv_status rope_store(const pkv_pool *pool, int32_t layer_id, const void *q, void *q_out,
+                      int32_t n_heads, const void *k_new, const void *v_new,
+                      const int32_t *position_ids, const float *freqs_cis, int64_t max_pos,
+                      int32_t rope_dim, const int32_t *out_cache_loc, int64_t n_new,
+                      void *stream) {
   pkv_status st = check_pool(pool, layer_id);
   if (st != PKV_OK) return st;
   if (n_new < 0 || max_pos <= 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0)
     return PKV_ERR_SHAPE;
-  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!dims_ok(pool)) return PKV_ERR_UNSUPPORTED;
+  // the rotated tail and the unrotated head of a row are whole 16-byte pieces
+  const int32_t piece = pool->dtype == PKV_BF16 ? 8 : 4;
+  if (rope_dim <= 0 || rope_dim > pool->head_dim || rope_dim % piece != 0) return PKV_ERR_SHAPE;
   if (n_new == 0) return PKV_OK;
   if (!q || !q_out || !k_new || !v_new || !position_ids || !freqs_cis || !out_cache_loc)
     return PKV_ERR_NULL;
@@ -731,8 +759,8 @@ pkv_status pkv_rope_kv_store(const pkv_pool *pool, int32_t layer_id, const void 
   a.q_out = q_out;
   a.k_new = k_new;
   a.v_new = v_new;
-  a.k_layer = const_cast<char *>(layer_ptr(pool->k_buffer, pool, layer_id));
-  a.v_layer = const_cast<char *>(layer_ptr(pool->v_buffer, pool, layer_id));
+  a.k_layer = const_cast<char *>(k_layer_ptr(pool, layer_id));
+  a.v_layer = const_cast<char *>(v_layer_ptr(pool, layer_id));
   a.position_ids = position_ids;
   a.freqs = freqs_cis;
   a.max_pos = max_pos;
@@ -741,8 +769,33 @@ pkv_status pkv_rope_kv_store(const pkv_pool *pool, int32_t layer_id, const void 
   a.n_heads = n_heads;
   a.n_kv_heads = pool->n_kv_heads;
   a.head_dim = pool->head_dim;
+  a.v_head_dim = v_dim(pool);
+  a.rope_dim = rope_dim;
   return hip_status(pkv::launch_rope_kv_store(a, pool->dtype == PKV_BF16 ? 1 : 0,
                                               (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_rope_kv_store(const pkv_pool *pool, int32_t layer_id, const void *q, void *q_out,
+                             int32_t n_heads, const void *k_new, const void *v_new,
+                             const int32_t *position_ids, const float *freqs_cis,
+                             int64_t max_pos, const int32_t *out_cache_loc, int64_t n_new,
+                             void *stream) {
+  if (!pool) return PKV_ERR_NULL;
+  return rope_store(pool, layer_id, q, q_out, n_heads, k_new, v_new, position_ids, freqs_cis,
+                    max_pos, pool->head_dim, out_cache_loc, n_new, stream);
+}
+
+pkv_status pkv_rope_kv_store_partial(const pkv_pool *pool, int32_t layer_id, const void *q,
+                                     void *q_out, int32_t n_heads, const void *k_new,
+                                     const void *v_new, const int32_t *position_ids,
+                                     const float *freqs_cis, int64_t max_pos, int32_t rope_dim,
+                                     const int32_t *out_cache_loc, int64_t n_new, void *stream) {
+  return rope_store(pool, layer_id, q, q_out, n_heads, k_new, v_new, position_ids, freqs_cis,
+                    max_pos, rope_dim, out_cache_loc, n_new, stream);
 }
 
 pkv_status pkv_paged_decode_merge(int32_t batch, int32_t n_heads, int32_t head_dim,
@@ -778,15 +831,15 @@ pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_s
   if (!step || !q || !out) return PKV_ERR_NULL;
   if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || step->batch > 65535)
     return PKV_ERR_SHAPE;
-  if (pool->head_dim != 64 && pool->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!dims_ok(pool)) return PKV_ERR_UNSUPPORTED;
   // the kernel ranks raw scores (the scale is applied in the exponent)
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.f)) return PKV_ERR_SHAPE;
   if (step->batch == 0 || step->n_new == 0) return PKV_OK;
   if (!step->req_pool_indices || !step->qo_indptr || !step->kv_indptr) return PKV_ERR_NULL;
   if (step->max_q_len <= 0 || step->max_q_len > pool->max_ctx_len) return PKV_ERR_SHAPE;
   pkv::PrefillArgs a{};
-  a.k_layer = layer_ptr(pool->k_buffer, pool, layer_id);
-  a.v_layer = layer_ptr(pool->v_buffer, pool, layer_id);
+  a.k_layer = k_layer_ptr(pool, layer_id);
+  a.v_layer = v_layer_ptr(pool, layer_id);
   set_table(a, pool);
   a.req_pool_indices = step->req_pool_indices;
   a.qo_indptr = step->qo_indptr;
@@ -806,7 +859,7 @@ pkv_status pkv_paged_prefill(const pkv_pool *pool, int32_t layer_id, const pkv_s
   a.max_q_len = step->max_q_len;
   a.causal = causal ? 1 : 0;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  return hip_status(pkv::launch_paged_prefill(a, pool->head_dim, (hipStream_t)stream));
+  return hip_status(pkv::launch_paged_prefill(a, pool->head_dim, v_dim(pool), (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -81,10 +81,10 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-template <int D>
+template <int DK, int DV>
 struct Smem {
-  static constexpr int KS = D + 8;   // K row stride (elements), 16-byte pad
-  static constexpr int VS = D + 32;  // V row stride (elements), 64-byte pad
+  static constexpr int KS = DK + 8;   // K row stride (elements), 16-byte pad
+  static constexpr int VS = DV + 32;  // V row stride (elements), 64-byte pad
   uint16_t k[BN * KS];
   uint16_t v[BN * VS];
 };
@@ -96,16 +96,26 @@ __device__ __forceinline__ int rows_of(const PrefillArgs &a, int i) {
 
 // OFF32: every row of the layer lies within 4 GiB of the layer base, so row
 // addresses are a uniform 64-bit base plus a 32-bit byte offset.  PAGED: the
-// table holds page ids of pages of 2^page_shift tokens (else slot ids).
-template <int D, bool OFF32, bool PAGED>
+// table holds page ids of pages of 2^page_shift tokens (else slot ids).  DK:
+// width of the query and key rows; DV: of the value and output rows (MLA
+// layers: keys qk_nope + qk_rope wide, values narrower).
+template <int DK, int DV, bool OFF32, bool PAGED>
 __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
-  constexpr int KS = Smem<D>::KS;
-  constexpr int VS = Smem<D>::VS;
-  constexpr int KSTEPS = D / 16;             // MFMA steps over head_dim for S^T
-  constexpr int DBLK = D / 32;               // 32-dim blocks of O^T
-  constexpr int KPIECES = BN * D / 8 / NT;   // 16-byte K (and V) pieces per thread per tile
-  static_assert(KPIECES >= 1, "staging split");
-  __shared__ Smem<D> sm[NBUF];
+  using SM = Smem<DK, DV>;
+  constexpr int KS = SM::KS;
+  constexpr int VS = SM::VS;
+  constexpr int KSTEPS = DK / 16;            // MFMA steps over the key width for S^T
+  // K fragments of a 32-key block are read in runs of KRUN steps before
+  // their products (all of them for keys up to 128 wide)
+  constexpr int KRUN = KSTEPS > 8 ? 4 : KSTEPS;
+  static_assert(KSTEPS % KRUN == 0, "fragment runs");
+  constexpr int DBLK = DV / 32;              // 32-dim blocks of O^T
+  constexpr int KPK = BN * DK / 8 / NT;      // 16-byte K pieces per thread per tile
+  constexpr int KPV = BN * DV / 8 / NT;      // 16-byte V pieces per thread per tile
+  constexpr bool SAME = DK == DV;            // then one slot id serves a K and a V piece
+  constexpr int NSLOT = SAME ? KPK : KPK + KPV;
+  static_assert(KPK >= 1 && KPV >= 1, "staging split");
+  __shared__ SM sm[NBUF];
 
   // Workgroups are dispatched to the 8 XCDs round-robin by linear id; taking
   // the kv-head from the low part of the id keeps every workgroup of one
@@ -163,27 +173,29 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   uint4 qf[KSTEPS];
   {
     const uint16_t *qrow =
-        reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(q0 + t) * a.n_heads + h) * D + 8 * half;
+        reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)(q0 + t) * a.n_heads + h) * DK + 8 * half;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
       qf[s] = row_ok ? load16(qrow + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
   }
 
   const int32_t *table = a.req_to_token + (int64_t)a.req_pool_indices[i] * a.table_stride;
-  const uint32_t row_bytes = (uint32_t)a.n_kv_heads * D * 2;
-  const char *kbase = reinterpret_cast<const char *>(a.k_layer) + (int64_t)hk * D * 2;
-  const char *vbase = reinterpret_cast<const char *>(a.v_layer) + (int64_t)hk * D * 2;
-  auto row_addr = [&](const char *base, int slot, uint32_t col_bytes) -> const char * {
+  const uint32_t krow_bytes = (uint32_t)a.n_kv_heads * DK * 2;
+  const uint32_t vrow_bytes = (uint32_t)a.n_kv_heads * DV * 2;
+  const char *kbase = reinterpret_cast<const char *>(a.k_layer) + (int64_t)hk * DK * 2;
+  const char *vbase = reinterpret_cast<const char *>(a.v_layer) + (int64_t)hk * DV * 2;
+  auto row_addr = [&](const char *base, uint32_t row_bytes, int slot,
+                      uint32_t col_bytes) -> const char * {
     if constexpr (OFF32)
       return base + ((uint32_t)slot * row_bytes + col_bytes);
     else
       return base + ((int64_t)slot * row_bytes + col_bytes);
   };
 
-  // Global -> register staging of one tile: every thread copies KPIECES
-  // 16-byte pieces of K and the same pieces of V (16 lanes per key row), so
-  // one slot id serves both.
-  uint4 kreg[KPIECES], vreg[KPIECES];
+  // Global -> register staging of one tile: every thread copies KPK 16-byte
+  // pieces of K and KPV of V (16 lanes per 128-dim row); with equal widths
+  // one slot id serves a K and a V piece.
+  uint4 kreg[KPK], vreg[KPV];
 
   // Slot ids are loaded one tile ahead of the rows they address, so a
   // tile's K/V loads never wait on a table load.  They are issued before the
@@ -191,7 +203,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   // the next fetch's wait for its slot ids leaves these rows in flight.  Keys
   // past kv_end read the last valid key instead (always masked), keeping
   // every load unconditional.
-  int slot[KPIECES];
+  int slot[NSLOT];
   auto slot_of = [&](int j) {
     const uint32_t pos = (uint32_t)min(j, kv_end - 1);
     if constexpr (PAGED)
@@ -199,32 +211,49 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
     else
       return table[pos];
   };
-  auto load_slots = [&](int tile, int(&ks)[KPIECES]) {
+  auto load_slots = [&](int tile, int(&ks)[NSLOT]) {
     const int base = tile * BN;
 #pragma unroll
-    for (int p = 0; p < KPIECES; ++p) ks[p] = slot_of(base + (tid + NT * p) / (D / 8));
+    for (int p = 0; p < KPK; ++p) ks[p] = slot_of(base + (tid + NT * p) / (DK / 8));
+    if constexpr (!SAME) {
+#pragma unroll
+      for (int p = 0; p < KPV; ++p) ks[KPK + p] = slot_of(base + (tid + NT * p) / (DV / 8));
+    }
   };
   auto fetch = [&](int tile) __attribute__((always_inline)) {
-    int ns[KPIECES];
+    int ns[NSLOT];
     load_slots(tile + 1, ns);
     __builtin_amdgcn_sched_barrier(0);  // keep the issue order: slot ids, then rows
 #pragma unroll
-    for (int p = 0; p < KPIECES; ++p) {
-      const uint32_t dg = (tid + NT * p) % (D / 8);
-      kreg[p] = load16(row_addr(kbase, slot[p], dg * 16));
-      vreg[p] = load16(row_addr(vbase, slot[p], dg * 16));
+    for (int p = 0; p < KPK; ++p) {
+      const uint32_t dg = (tid + NT * p) % (DK / 8);
+      kreg[p] = load16(row_addr(kbase, krow_bytes, slot[p], dg * 16));
+      if constexpr (SAME) vreg[p] = load16(row_addr(vbase, vrow_bytes, slot[p], dg * 16));
+    }
+    if constexpr (!SAME) {
+#pragma unroll
+      for (int p = 0; p < KPV; ++p) {
+        const uint32_t dg = (tid + NT * p) % (DV / 8);
+        vreg[p] = load16(row_addr(vbase, vrow_bytes, slot[KPK + p], dg * 16));
+      }
     }
 #pragma unroll
-    for (int p = 0; p < KPIECES; ++p) slot[p] = ns[p];
+    for (int p = 0; p < NSLOT; ++p) slot[p] = ns[p];
   };
 
-  auto stash = [&](Smem<D> &buf) __attribute__((always_inline)) {
+  auto stash = [&](SM &buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < KPIECES; ++p) {
+    for (int p = 0; p < KPK; ++p) {
       const int piece = tid + NT * p;
-      const int key = piece / (D / 8);
-      const int dg = piece - key * (D / 8);
+      const int key = piece / (DK / 8);
+      const int dg = piece - key * (DK / 8);
       store16(&buf.k[key * KS + dg * 8], kreg[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < KPV; ++p) {
+      const int piece = tid + NT * p;
+      const int key = piece / (DV / 8);
+      const int dg = piece - key * (DV / 8);
       store16(&buf.v[key * VS + dg * 8], vreg[p]);
     }
   };
@@ -251,21 +280,26 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   // S^T of one 64-key tile (two 32-key blocks).  All fragment reads of a
   // block are issued before its products, so the products do not wait on
   // LDS latency one read at a time.
-  auto qk = [&](const Smem<D> &buf, f32x16_t(&sacc)[2]) __attribute__((always_inline)) {
+  auto qk = [&](const SM &buf, f32x16_t(&sacc)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const uint16_t *krow = &buf.k[(kb * 32 + col) * KS + 8 * half];
-      uint4 kf[KSTEPS];
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) kf[s] = *reinterpret_cast<const uint4 *>(krow + 16 * s);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int r0 = 0; r0 < KSTEPS; r0 += KRUN) {
+        uint4 kf[KRUN];
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) sacc[kb] = mfma32(kf[s], qf[s], s == 0 ? zero16 : sacc[kb]);
+        for (int s = 0; s < KRUN; ++s)
+          kf[s] = *reinterpret_cast<const uint4 *>(krow + 16 * (r0 + s));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KRUN; ++s)
+          sacc[kb] = mfma32(kf[s], qf[r0 + s], r0 + s == 0 ? zero16 : sacc[kb]);
+      }
     }
   };
 
   // (Mask,) online softmax of one tile's S^T, then O^T += V^T P^T.
-  auto softmax_pv = [&](int tile, f32x16_t(&sacc)[2], const Smem<D> &buf,
+  auto softmax_pv = [&](int tile, f32x16_t(&sacc)[2], const SM &buf,
                         auto masked) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(masked)::value;
     if constexpr (MASK) {
@@ -399,7 +433,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   const float l_run = l_lane + __shfl_xor(l_lane, 32);
   if (!row_ok) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((int64_t)(q0 + t) * a.n_heads + h) * D;
+  uint16_t *orow = reinterpret_cast<uint16_t *>(a.out) + ((int64_t)(q0 + t) * a.n_heads + h) * DV;
 #pragma unroll
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -412,7 +446,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
     }
 }
 
-template <int D>
+template <int DK, int DV>
 hipError_t launch_d(const PrefillArgs &a, bool off32, hipStream_t stream) {
   const int64_t row_blocks = ((int64_t)a.max_q_len * a.group + BM - 1) / BM;
   if (row_blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -423,23 +457,26 @@ hipError_t launch_d(const PrefillArgs &a, bool off32, hipStream_t stream) {
   const dim3 grid((uint32_t)blocks);
   const bool paged = a.page_shift > 0;
   if (off32 && !paged)
-    hipLaunchKernelGGL((prefill_kernel<D, true, false>), grid, dim3(NT), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<DK, DV, true, false>), grid, dim3(NT), 0, stream, args);
   else if (off32)
-    hipLaunchKernelGGL((prefill_kernel<D, true, true>), grid, dim3(NT), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<DK, DV, true, true>), grid, dim3(NT), 0, stream, args);
   else if (!paged)
-    hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, dim3(NT), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<DK, DV, false, false>), grid, dim3(NT), 0, stream, args);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, false, true>), grid, dim3(NT), 0, stream, args);
+    hipLaunchKernelGGL((prefill_kernel<DK, DV, false, true>), grid, dim3(NT), 0, stream, args);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, hipStream_t stream) {
+hipError_t launch_paged_prefill(const PrefillArgs &a, int head_dim, int v_head_dim,
+                                hipStream_t stream) {
+  // Offsets fit 32 bits when the wider (key) rows of the whole layer do.
   const uint64_t layer_bytes = (uint64_t)a.pool_size * a.n_kv_heads * head_dim * 2;
   const bool off32 = layer_bytes <= 0xffffffffull;
-  if (head_dim == 128) return launch_d<128>(a, off32, stream);
-  if (head_dim == 64) return launch_d<64>(a, off32, stream);
+  if (head_dim == 128 && v_head_dim == 128) return launch_d<128, 128>(a, off32, stream);
+  if (head_dim == 64 && v_head_dim == 64) return launch_d<64, 64>(a, off32, stream);
+  if (head_dim == 192 && v_head_dim == 128) return launch_d<192, 128>(a, off32, stream);
   return hipErrorInvalidValue;
 }
 

@@ -78,9 +78,12 @@ __device__ __forceinline__ uint4 rotate(const uint4 &w, const float *f) {
   return Piece<T>::store(y);
 }
 
-// One thread per 16-byte piece.  Threads [0, q_pieces) rotate query pieces
+// One thread per 16-byte piece.  Threads [0, q_pieces) handle query pieces
 // (token i, head h, piece c in row order); the next kv_pieces threads each
-// rotate one key piece into the pool and copy the matching value piece.
+// handle one key piece, written to the pool, and the matching value piece
+// where the value row is that wide.  Pieces in the last rope_dim dims of a
+// row are rotated (table entry (c * E - (head_dim - rope_dim)) / 2 onwards);
+// the others are copied unchanged (MLA rows: only the qk_rope part turns).
 // Consecutive threads cover consecutive pieces of a row, so every row is one
 // coalesced run.  Positions outside [0, max_pos) read the nearest table row
 // (the caller guarantees valid positions; the clamp only keeps reads in
@@ -90,29 +93,38 @@ __global__ void __launch_bounds__(256) rope_kv_store_kernel(const RopeArgs a, in
                                                             int64_t kv_pieces) {
   constexpr int E = Piece<T>::E;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int ppr = a.head_dim / E;  // pieces per head row
+  const int ppr = a.head_dim / E;      // pieces per query / key row
+  const int vppr = a.v_head_dim / E;   // pieces per value row
+  const int first_rot = (a.head_dim - a.rope_dim) / E;  // first rotated piece
   if (t < q_pieces) {
     const int64_t row = t / ppr;
     const int c = (int)(t - row * ppr);
-    const int64_t i = row / a.n_heads;
-    const int64_t p = min(max((int64_t)a.position_ids[i], (int64_t)0), a.max_pos - 1);
-    const float *f = a.freqs + p * a.head_dim + (int64_t)c * E;
     const uint4 w = reinterpret_cast<const uint4 *>(a.q)[t];
-    reinterpret_cast<uint4 *>(a.q_out)[t] = rotate<T>(w, f);
+    uint4 r = w;
+    if (c >= first_rot) {
+      const int64_t i = row / a.n_heads;
+      const int64_t p = min(max((int64_t)a.position_ids[i], (int64_t)0), a.max_pos - 1);
+      r = rotate<T>(w, a.freqs + p * a.rope_dim + (int64_t)(c - first_rot) * E);
+    }
+    reinterpret_cast<uint4 *>(a.q_out)[t] = r;
   } else if (t < q_pieces + kv_pieces) {
     const int64_t u = t - q_pieces;
     const int64_t row = u / ppr;
     const int c = (int)(u - row * ppr);
     const int64_t i = row / a.n_kv_heads;
     const int64_t hk = row - i * a.n_kv_heads;
-    const int64_t p = min(max((int64_t)a.position_ids[i], (int64_t)0), a.max_pos - 1);
-    const float *f = a.freqs + p * a.head_dim + (int64_t)c * E;
     const int64_t loc = a.out_cache_loc[i];
-    const int64_t dst = (loc * a.n_kv_heads + hk) * ppr + c;
     const uint4 kw = reinterpret_cast<const uint4 *>(a.k_new)[u];
-    const uint4 vw = reinterpret_cast<const uint4 *>(a.v_new)[u];
-    reinterpret_cast<uint4 *>(a.k_layer)[dst] = rotate<T>(kw, f);
-    reinterpret_cast<uint4 *>(a.v_layer)[dst] = vw;
+    uint4 kr = kw;
+    if (c >= first_rot) {
+      const int64_t p = min(max((int64_t)a.position_ids[i], (int64_t)0), a.max_pos - 1);
+      kr = rotate<T>(kw, a.freqs + p * a.rope_dim + (int64_t)(c - first_rot) * E);
+    }
+    reinterpret_cast<uint4 *>(a.k_layer)[(loc * a.n_kv_heads + hk) * ppr + c] = kr;
+    if (c < vppr) {
+      const uint4 vw = reinterpret_cast<const uint4 *>(a.v_new)[row * vppr + c];
+      reinterpret_cast<uint4 *>(a.v_layer)[(loc * a.n_kv_heads + hk) * vppr + c] = vw;
+    }
   }
 }
 

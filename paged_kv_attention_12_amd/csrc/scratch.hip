@@ -57,7 +57,9 @@ pkv_status pkv_paged_decode_store_noalloc(const pkv_pool *pool, int32_t layer_id
   if (step->batch < 0 || n_heads <= 0 || num_splits <= 0) return PKV_ERR_SHAPE;
   if (step->batch == 0) return PKV_OK;
   const size_t need =
-      pkv_decode_workspace_bytes(step->batch, n_heads, pool->head_dim, num_splits);
+      pkv_decode_workspace_bytes(step->batch, n_heads,
+                                 pool->v_head_dim > 0 ? pool->v_head_dim : pool->head_dim,
+                                 num_splits);
   if (need == 0) return PKV_ERR_SHAPE;
   if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH_LIMIT;
   void *ws = nullptr;
