@@ -168,6 +168,12 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   const int ntiles = (kv_end + BN - 1) / BN;
   const int wg_min_lim = a.causal ? prefix + (rb * BM) / G + 1 : kv_len;
   const int n_free = min(ntiles, wg_min_lim / BN);
+  // Keys any row of this wavefront sees: in the tiles that need the mask, a
+  // 32-key block at or past this limit is masked for all 32 rows, and its
+  // products and weights are skipped.
+  const int w_first = rb * BM + wave * WROWS;
+  const int w_last = min(rows, w_first + WROWS) - 1;
+  const int wave_lim = w_last < w_first ? 0 : (a.causal ? prefix + w_last / G + 1 : kv_len);
 
   // Q (B operand of S^T): lane holds dims 16s + 8*half .. +8 of its row for step s.
   uint4 qf[KSTEPS];
@@ -279,10 +285,19 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
 
   // S^T of one 64-key tile (two 32-key blocks).  All fragment reads of a
   // block are issued before its products, so the products do not wait on
-  // LDS latency one read at a time.
-  auto qk = [&](const SM &buf, f32x16_t(&sacc)[2]) __attribute__((always_inline)) {
+  // LDS latency one read at a time.  In a tile that needs the mask, a block
+  // past every row of the wavefront is set to -inf without its products.
+  const f32x16_t ninf16 = {kNegInf, kNegInf, kNegInf, kNegInf, kNegInf, kNegInf, kNegInf, kNegInf,
+                           kNegInf, kNegInf, kNegInf, kNegInf, kNegInf, kNegInf, kNegInf, kNegInf};
+  auto qk = [&](const SM &buf, f32x16_t(&sacc)[2], int tile,
+                auto masked) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      if (MASK && tile * BN + 32 * kb >= wave_lim) {
+        sacc[kb] = ninf16;  // every key of the block is past every row of this wave
+        continue;
+      }
       const uint16_t *krow = &buf.k[(kb * 32 + col) * KS + 8 * half];
 #pragma unroll
       for (int r0 = 0; r0 < KSTEPS; r0 += KRUN) {
@@ -345,6 +360,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
     for (int ts = 0; ts < 4; ++ts) {
       const int kb = ts >> 1;
       const int x0 = 8 * (ts & 1);
+      if (MASK && tile * BN + 32 * kb >= wave_lim) continue;  // weights all 0
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(sacc[kb][x0 + e], c2, -mc));
@@ -395,7 +411,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
   if (wave < 4) {
     auto period = [&](int k, auto masked) __attribute__((always_inline)) {
       const int nb = next_buf(cur);
-      qk(sm[cur], sacc);
+      qk(sm[cur], sacc, k, masked);
       stash(sm[nb]);
       fetch(k + 2);
       softmax_pv(k, sacc, sm[cur], masked);
@@ -412,7 +428,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
       softmax_pv(k - 1, sacc, sm[prev], masked);
       stash(sm[nb]);
       fetch(k + 2);
-      qk(sm[cur], sacc);
+      qk(sm[cur], sacc, k, masked);
       lds_barrier();
       prev = cur;
       cur = nb;
@@ -420,7 +436,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillArgs a) {
     // period 0: no earlier tile to finish
     stash(sm[1]);
     fetch(2);
-    qk(sm[0], sacc);
+    if (n_free > 0)
+      qk(sm[0], sacc, 0, std::false_type{});
+    else
+      qk(sm[0], sacc, 0, std::true_type{});
     lds_barrier();
     prev = 0;
     cur = 1;
