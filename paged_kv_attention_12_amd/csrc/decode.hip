@@ -262,11 +262,10 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
 // (m, l, o) of up to KB splits in one batch, the row maximum is reduced over
 // the workgroup, then every thread weighs what it holds: one memory round
 // trip for up to SG * KB splits.  Group sums are added through LDS.
-template <typename T, int D>
+template <typename T, int D, int KB>
 __global__ void __launch_bounds__(256) decode_merge_kernel(const MergeArgs a) {
   constexpr int TPR = D / 4;
   constexpr int SG = 256 / TPR;
-  constexpr int KB = 16;
   __shared__ float s_red[4];
   __shared__ float4 s_num[SG][TPR];
   __shared__ float s_den[SG];
@@ -1038,6 +1037,18 @@ hipError_t decode_dispatch_ng(const DecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Few rows (a decode step of few requests): batches of 16 splits per thread,
+// one memory round trip for up to 128 splits of 128-dim rows.  Many rows:
+// batches of 8, whose registers (76 against 126) let half again as many
+// workgroups stay resident, for rows that mostly hold few splits.
+template <typename T, int D>
+void merge_d(const MergeArgs &a, hipStream_t stream) {
+  if (a.rows > 1024)
+    hipLaunchKernelGGL((decode_merge_kernel<T, D, 8>), dim3(a.rows), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<T, D, 16>), dim3(a.rows), dim3(256), 0, stream, a);
+}
+
 }  // namespace
 
 bool decode_mfma_shape(int dtype, int head_dim, int v_head_dim) {
@@ -1124,17 +1135,16 @@ hipError_t launch_decode_prefix(const PrefixArgs &args, hipStream_t stream) {
 }
 
 hipError_t launch_decode_merge(const MergeArgs &a, int dtype, int head_dim, hipStream_t stream) {
-  const dim3 grid(a.rows);
   if (dtype == 1) {
     if (head_dim == 128)
-      hipLaunchKernelGGL((decode_merge_kernel<uint16_t, 128>), grid, dim3(256), 0, stream, a);
+      merge_d<uint16_t, 128>(a, stream);
     else
-      hipLaunchKernelGGL((decode_merge_kernel<uint16_t, 64>), grid, dim3(256), 0, stream, a);
+      merge_d<uint16_t, 64>(a, stream);
   } else {
     if (head_dim == 128)
-      hipLaunchKernelGGL((decode_merge_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+      merge_d<float, 128>(a, stream);
     else
-      hipLaunchKernelGGL((decode_merge_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+      merge_d<float, 64>(a, stream);
   }
   return hipGetLastError();
 }
