@@ -335,12 +335,23 @@ int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_head
   const int64_t work = total_len * n_kv_heads * chunks;
   // Equal lengths: about 1024 long-running wavefronts (one per SIMD) keep the
   // per-split start-up and merge cost low.  Ragged lengths: short splits of at
-  // most 256 tokens, about 16K of them, so that the device balances the load.
+  // most 256 tokens, about 8K of them (eight per SIMD), so that the device
+  // balances the load; twice as many measured slower (each split pays the
+  // start-up chain again).
   const bool ragged = (int64_t)batch * max_len > total_len + total_len / 4;
-  int64_t chunk = ragged ? std::min<int64_t>(256, work / 16384)
+  int64_t chunk = ragged ? std::min<int64_t>(256, work / 8192)
                          : std::min<int64_t>(2048, work / 1024);
   chunk = std::max<int64_t>(chunk, 16);
   int64_t s = ((int64_t)max_len + chunk - 1) / chunk;
+  // Ragged batches: the dispatcher deals workgroups to the 8 XCDs round-robin
+  // in grid order (four kv-heads of one split, then the next split, then the
+  // next request).  When a request's workgroups are a multiple of 8, split s
+  // of every request lands on the same XCDs, and the XCDs of the low split
+  // indices, which every request has, get the most work.  One split more
+  // moves each request's splits onto other XCDs.  (With a multiple of 8
+  // workgroups per split, every split already covers all XCDs alike.)
+  const int64_t wgs = (n_kv_heads * chunks + 3) / 4;  // workgroups per split
+  if (ragged && batch > 1 && wgs % 8 != 0 && (wgs * s) % 8 == 0) ++s;
   s = std::min<int64_t>(s, max_splits);
   s = std::min<int64_t>(s, 65535);
   return (int32_t)std::max<int64_t>(1, s);
