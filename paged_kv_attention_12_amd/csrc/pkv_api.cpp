@@ -345,13 +345,15 @@ int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_head
   int64_t s = ((int64_t)max_len + chunk - 1) / chunk;
   // Ragged batches: the dispatcher deals workgroups to the 8 XCDs round-robin
   // in grid order (four kv-heads of one split, then the next split, then the
-  // next request).  When a request's workgroups are a multiple of 8, split s
-  // of every request lands on the same XCDs, and the XCDs of the low split
-  // indices, which every request has, get the most work.  One split more
-  // moves each request's splits onto other XCDs.  (With a multiple of 8
-  // workgroups per split, every split already covers all XCDs alike.)
+  // next request), so request b's split s starts on XCD (b * w + s * wgs) % 8
+  // with w = wgs * num_splits workgroups per request.  When w is a multiple
+  // of 8, split s of every request lands on the same XCDs, and the XCDs of
+  // the low split indices, which every request has, get the most work.  An
+  // odd split count makes w carry the fewest factors of 2 it can, spreading
+  // the requests' splits over the most XCD offsets (with a multiple of 8
+  // workgroups per split, every split already covers all XCDs alike).
   const int64_t wgs = (n_kv_heads * chunks + 3) / 4;  // workgroups per split
-  if (ragged && batch > 1 && wgs % 8 != 0 && (wgs * s) % 8 == 0) ++s;
+  if (ragged && batch > 1 && wgs % 8 != 0 && s % 2 == 0) ++s;
   s = std::min<int64_t>(s, max_splits);
   s = std::min<int64_t>(s, 65535);
   return (int32_t)std::max<int64_t>(1, s);
