@@ -305,14 +305,17 @@ def kernel_launch_spread(runner, launches=100, warm=False):
 # ---------------------------------------------------------------------------
 # graph-captured decode loop: one token of a 32-layer forward per replay
 # ---------------------------------------------------------------------------
-def bench_decode_loop(L, tokens=8):
-    """Per token, for every layer (31 .. 0): the rotary embedding fused with
-    the K/V write of the new token, the split attention and the merge; then
-    the in-place advance of the step metadata (seq_lens, position_ids,
-    out_cache_loc, kv_indptr).  Captured once, replayed token after token.
-    The request starts at position L - tokens - 1, so the table row (L
-    positions) covers every token and the last advance.  Also timed: the
-    same launches issued eagerly from Python through the C ABI."""
+def bench_decode_loop(L, tokens=8, fused=True):
+    """Per token, for every layer (31 .. 0): the rotary embedding of the new
+    token with its K/V write, the split attention and the merge; then the
+    in-place advance of the step metadata (seq_lens, position_ids,
+    out_cache_loc, kv_indptr).  fused: the rotation and the write inside the
+    split kernel (pkv_paged_decode_rope_store, two launches a layer); else
+    pkv_rope_kv_store, then the split and merge launches (three a layer).
+    Captured once, replayed token after token.  The request starts at
+    position L - tokens - 1, so the table row (L positions) covers every
+    token and the last advance.  Also timed: the same launches issued
+    eagerly from Python through the C ABI."""
     import torch
     import workloads as W
     from paged_kv_attention_12_amd import api
@@ -331,6 +334,10 @@ def bench_decode_loop(L, tokens=8):
 
     def one_token():
         for layer in range(c.n_layers - 1, -1, -1):
+            if fused:
+                api.rope_decode_step(kb, vb, tab, layer, step, t["q"], t["k_new"], t["v_new"],
+                                     freqs, c.sm_scale, num_splits=ns, workspace=ws, out=out)
+                continue
             api.rope_kv_store(kb, vb, tab, layer, step, t["q"], t["k_new"], t["v_new"], freqs,
                               q_out=q_rot)
             api.decode_step(kb, vb, tab, layer, step, q_rot, None, None, c.sm_scale,
@@ -377,7 +384,8 @@ def bench_decode_loop(L, tokens=8):
     del g, r
     torch.cuda.empty_cache()
     n = c.n_layers
-    return {"tokens": tokens, "layers": n, "context": [p0 + 1, p0 + tokens],
+    return {"form": "rope_in_step" if fused else "rope_then_step", "tokens": tokens,
+            "layers": n, "context": [p0 + 1, p0 + tokens],
             "graph_us_per_token": graph * 1e6, "graph_us_per_layer": graph / n * 1e6,
             "eager_us_per_token": eager * 1e6, "eager_us_per_layer": eager / n * 1e6,
             "metadata_advanced": advanced}
@@ -797,9 +805,12 @@ def main():
 
         log("graph-captured decode loop")
         extra["decode_loop"] = {str(L): bench_decode_loop(L) for L in (1024, 32768)}
-        for L, v in extra["decode_loop"].items():
-            log(f"  L={L}: graph {v['graph_us_per_layer']:.1f} us/layer, eager "
-                f"{v['eager_us_per_layer']:.1f} us/layer, advanced={v['metadata_advanced']}")
+        extra["decode_loop_rope_then_step"] = {str(L): bench_decode_loop(L, fused=False)
+                                               for L in (1024, 32768)}
+        for key in ("decode_loop", "decode_loop_rope_then_step"):
+            for L, v in extra[key].items():
+                log(f"  {v['form']} L={L}: graph {v['graph_us_per_layer']:.1f} us/layer, eager "
+                    f"{v['eager_us_per_layer']:.1f} us/layer, advanced={v['metadata_advanced']}")
 
         # the same workloads on pools of 64-token pages
         log("paged pools (64-token pages)")

@@ -428,6 +428,37 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
                                   void *workspace, size_t ws_bytes, void *out, void *stream);
 
 /* ----------------------------------------------------------------------
+ * The decode step of pkv_rope_kv_store followed by pkv_paged_decode_store,
+ * in two launches ("Inference" guide, section "Rotary Embedding Backend":
+ * the query and the new key are rotated by the freqs_cis row of their
+ * position before the cache write and the attention; section "KV Cache";
+ * section "Attention Backend").  q and k_new arrive unrotated:
+ *   q'[b] = rot(q[b], position_ids[b]), k'[b] = rot(k_new[b], position_ids[b])
+ *   k_buffer[layer, out_cache_loc[b]] = k'[b], v_buffer[...] = v_new[b],
+ *   out[b, h] = sum_j softmax_j(q'[b,h] . k_j * sm_scale) v_j
+ * over the seq_lens[b] keys of request b, the new one included, with rot
+ * the rotation of pkv_rope_kv_store (fp32, rounded once to bf16), so the
+ * output and the pool equal those of the two calls bit for bit; q' is not
+ * written anywhere.  Decode steps only (step->n_new == batch).  Pools of
+ * bf16 with head_dim and v_head_dim 128 and at most 16 query heads per
+ * kv-head; out_cache_loc[b] must be the slot of position seq_lens[b] - 1 of
+ * request b, with no other position read in this step mapped to it (the new
+ * rows are written to the pool before they are attended).
+ * position_ids: device int32 [batch]; freqs_cis: device f32
+ * [max_pos, 64, 2], 16-byte aligned; workspace / num_splits as for
+ * pkv_paged_decode_store.
+ * Errors: as pkv_paged_decode_store and pkv_rope_kv_store, plus
+ * PKV_ERR_UNSUPPORTED for other pool shapes or more than 16 query heads per
+ * kv-head.
+ * ---------------------------------------------------------------------- */
+pkv_status pkv_paged_decode_rope_store(const pkv_pool *pool, int32_t layer_id,
+                                       const pkv_step *step, const void *q, const void *k_new,
+                                       const void *v_new, const int32_t *position_ids,
+                                       const float *freqs_cis, int64_t max_pos, int32_t n_heads,
+                                       float sm_scale, int32_t num_splits, void *workspace,
+                                       size_t ws_bytes, void *out, void *stream);
+
+/* ----------------------------------------------------------------------
  * The decode step of pkv_paged_decode_store without a caller workspace, for
  * callers that cannot allocate device memory (code under graph capture, tight
  * serving loops, harnesses that forbid hipMalloc).  Same arguments, result

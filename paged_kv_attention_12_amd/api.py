@@ -143,6 +143,26 @@ def stored_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: De
     return out
 
 
+def rope_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step: DeviceStep, q,
+                     k_new, v_new, freqs_cis, sm_scale: float, num_splits: Optional[int] = None,
+                     workspace=None, out=None):
+    """The decode step with the rotary turn of q and k_new folded into the
+    split kernel, then the merge (pkv_paged_decode_rope_store): q and k_new
+    unrotated, positions step.position_ids.  Returns out."""
+    H, d = int(q.shape[1]), int(v_buffer.shape[3])
+    if num_splits is None:
+        num_splits = B.pkv_decode_pick_splits(step.batch, int(k_buffer.shape[2]), H,
+                                              step.max_len, step.total_len)
+    if workspace is None:
+        workspace = decode_workspace(step.batch, H, d, num_splits, q.device)
+    if out is None:
+        out = q.new_empty((q.shape[0], q.shape[1], v_buffer.shape[3]))
+    B.pkv_paged_decode_rope_store(k_buffer, v_buffer, req_to_token, layer_id, step.c, q, k_new,
+                                  v_new, step.position_ids, freqs_cis, sm_scale, num_splits,
+                                  workspace, out, page_size=step.page_size)
+    return out
+
+
 class PrefixGroups:
     """The prefix groups of one decode step (pkv_decode_prefix_groups on the
     host copies of its metadata and table), copied to the device once."""

@@ -37,7 +37,7 @@ EXPORTED = (
     "pkv_paged_decode_step", "pkv_decode_step_pick_splits", "pkv_paged_decode_store",
     "pkv_build_positions", "pkv_rope_kv_store", "pkv_decode_advance", "pkv_prefill_blocks",
     "pkv_paged_decode_store_noalloc", "pkv_decode_prefix_groups", "pkv_paged_decode_shared",
-    "pkv_rope_kv_store_partial",
+    "pkv_rope_kv_store_partial", "pkv_paged_decode_rope_store",
 )
 
 PKV_PREFIX_GROUP_MAX = 16
@@ -131,6 +131,9 @@ def load() -> C.CDLL:
                                                 i64, i32, P, i64, P]),
         "pkv_decode_advance": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, P, P, P, P]),
         "pkv_prefill_blocks": (C.c_int, [i32, P, P, i32, i32, P, i64, C.POINTER(C.c_int64)]),
+        "pkv_paged_decode_rope_store": (C.c_int, [C.POINTER(pkv_pool), i32, C.POINTER(pkv_step),
+                                                  P, P, P, P, P, i64, i32, f32, i32, P, sz, P,
+                                                  P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -431,6 +434,30 @@ def pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id: int, step
         _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _dev_ptr(out, "out"), _stream())
     _check(st, "pkv_paged_decode_store")
+
+
+def pkv_paged_decode_rope_store(k_buffer, v_buffer, req_to_token, layer_id: int,
+                                step: pkv_step, q, k_new, v_new, position_ids, freqs_cis,
+                                sm_scale: float, num_splits: int, workspace, out,
+                                page_size: int = 1) -> None:
+    """The two-launch decode step with the rotary turn of q and k_new folded
+    in (pkv_paged_decode_rope_store)."""
+    import torch
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
+    _check_q_out(q, out, k_buffer, v_buffer, step.batch)
+    _check_new(k_new, v_new, k_buffer, v_buffer, step.batch)
+    if freqs_cis.dim() != 3 or tuple(freqs_cis.shape[1:]) != (int(k_buffer.shape[3]) // 2, 2) \
+            or freqs_cis.dtype != torch.float32:
+        raise ValueError("freqs_cis must be float32 [max_pos, head_dim / 2, 2]")
+    if position_ids.numel() != step.batch:
+        raise ValueError("position_ids must hold one entry per request")
+    st = load().pkv_paged_decode_rope_store(
+        C.byref(pool), int(layer_id), C.byref(step), _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"),
+        _dev_ptr(v_new, "v_new"), _dev_ptr(position_ids, "position_ids", torch.int32),
+        _dev_ptr(freqs_cis, "freqs_cis", torch.float32), int(freqs_cis.shape[0]),
+        int(q.shape[1]), float(sm_scale), int(num_splits), _dev_ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _dev_ptr(out, "out"), _stream())
+    _check(st, "pkv_paged_decode_rope_store")
 
 
 def pkv_paged_decode_store_noalloc(k_buffer, v_buffer, req_to_token, layer_id: int,

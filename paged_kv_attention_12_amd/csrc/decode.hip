@@ -417,12 +417,15 @@ constexpr int kKT = 32;      // keys per iteration of a wavefront
 // kSlotTile).  On return o[e][i] holds the
 // unnormalised O[column c][32g + 8i + e] against the base-2 running max m_run,
 // and l_tot the running sum (both per column, equal in the four lane groups).
-template <int TS, bool NEW, int P, int DK = kMfmaD>
+template <int TS, bool NEW, int P, int DK = kMfmaD, bool ROPE = false>
 __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot, int pool_row,
                                             int start, int end, int first, bool active, int hk,
                                             const uint16_t *qcol, const uint16_t *knew,
                                             const uint16_t *vnew, int newpos, f32x4_t (&o)[8],
-                                            float &m_run, float &l_tot) {
+                                            float &m_run, float &l_tot,
+                                            const float *rope_row = nullptr,
+                                            float *s_rope = nullptr, uint16_t *rope_dst = nullptr,
+                                            uint4 rope_piece = uint4{}) {
   constexpr int D = kMfmaD;  // value width
   constexpr int KS = DK / 32;  // 32-dim steps over the key width
   constexpr int KT = kKT;
@@ -452,6 +455,14 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
       if (256 * k < run_cap) s_slot[threadIdx.x + 256 * k] = sv[k];
   };
   load_run(start);  // first on the dependent chain to the K/V rows
+  // ROPE: the table row of the new token's position (DK floats), staged in
+  // LDS with the first run of slot ids.
+  float4 rope_v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (ROPE) {
+    static_assert(DK == kMfmaD, "rotary turn of 128-wide rows");
+    static_assert(!NEW, "with the rotary turn the new rows are written, then read as pool rows");
+    if (threadIdx.x < DK / 4) rope_v = reinterpret_cast<const float4 *>(rope_row)[threadIdx.x];
+  }
 
   // Q^T operand: column c, dims 8g + 32k .. +8 for step k.
   uint4 qf[KS];
@@ -570,7 +581,29 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
       load_run(r0);
     }
     store_run();
+    if constexpr (ROPE) {
+      if (r0 == start && threadIdx.x < DK / 4)
+        reinterpret_cast<float4 *>(s_rope)[threadIdx.x] = rope_v;
+    }
     __syncthreads();
+    if constexpr (ROPE) {
+      if (r0 == start) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) qf[k] = rotate_bf16x8(qf[k], s_rope + 8 * g + 32 * k);
+        // The new token's rows, written before any of them is fetched: lanes
+        // [0, DK/8) carry the key pieces (turned here), the next D/8 lanes the
+        // value pieces.  This wave is the only reader of its kv-head's rows of
+        // the split; the release / acquire pair orders the other lanes' later
+        // loads of those rows after the stores.
+        if (rope_dst) {
+          const uint4 piece =
+              lane < DK / 8 ? rotate_bf16x8(rope_piece, s_rope + 8 * lane) : rope_piece;
+          store16(rope_dst, piece);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      }
+    }
     if (!active) continue;
     const int round_tiles = (r1 - r0 + KT - 1) / KT;
     const int ntiles = first < round_tiles ? (round_tiles - first + TS - 1) / TS : 0;
@@ -598,14 +631,27 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
 // and the wavefront of head chunk 0 of each kv-head in the split holding that
 // position writes them to the pool slot out_cache_loc[b] (no wavefront of
 // the launch reads that pool row).
-template <bool NEW, int DK = kMfmaD>
+// With ROPE (NEW only) q and k_new arrive unrotated: every wavefront turns
+// its query rows by row position_ids[b] of the table (staged in s_rope), and
+// the wavefront of each kv-head in the split holding the new token writes the
+// turned key row and the value row to the pool before it fetches any row, so
+// the split reads them as pool rows (one wavefront per kv-head: at most 16
+// query heads per kv-head, and out_cache_loc[b] the slot of position
+// seq_lens[b] - 1).
+template <bool NEW, int DK = kMfmaD, bool ROPE = false>
 __device__ __forceinline__ void split_mfma_body(const StepArgs &sa, int32_t *s_slot, int b, int s,
-                                                int wx) {
+                                                int wx, float *s_rope = nullptr) {
   constexpr int D = kMfmaD;  // value width; keys are DK wide
   const DecodeArgs &a = sa.d;
+  static_assert(!ROPE || NEW, "the rotary turn comes with the new-token write");
 
   const int L = a.seq_lens[b];
   const int pool_row = a.req_pool_indices[b];
+  const float *rope_row = nullptr;
+  if constexpr (ROPE) {
+    const int64_t p = min(max((int64_t)sa.position_ids[b], (int64_t)0), sa.max_pos - 1);
+    rope_row = sa.freqs + p * D;
+  }
   // With a shared prefix the request's own splits start at kv_start[b].
   const int start = (a.kv_start ? a.kv_start[b] : 0) + s * a.chunk;
   const int end = split_end(a, s, start, L);
@@ -681,13 +727,20 @@ __device__ __forceinline__ void split_mfma_body(const StepArgs &sa, int32_t *s_s
   const uint16_t *qcol =
       col_ok ? reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)b * a.n_heads + h0 + c) * DK
              : nullptr;
-  if (NEW && start <= newpos && newpos < end)
+  if constexpr (ROPE) {
+    // The new rows go to the pool first (turned key, value), then every
+    // split reads pool rows only.
+    attend_mfma<1, false, kRing, DK, true>(a, s_slot, pool_row, start, end, 0, active, hk, qcol,
+                                           nullptr, nullptr, -1, o, m_run, l_tot, rope_row,
+                                           s_rope, writer ? new_dst : nullptr, new_piece);
+  } else if (NEW && start <= newpos && newpos < end) {
     attend_mfma<1, true, kRing, DK>(a, s_slot, pool_row, start, end, 0, active, hk, qcol, knew,
                                     vnew, newpos, o, m_run, l_tot);
-  else
+  } else {
     attend_mfma<1, false, kRing, DK>(a, s_slot, pool_row, start, end, 0, active, hk, qcol,
                                      nullptr, nullptr, -1, o, m_run, l_tot);
-  if (NEW && writer) store16(new_dst, new_piece);
+  }
+  if (NEW && !ROPE && writer) store16(new_dst, new_piece);
   if (!active || !col_ok) return;
   // Lane (c, g) holds O[head c][32g + 8i + e] in o[e][i].
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -709,6 +762,14 @@ template <bool NEW, int DK>
 __global__ void __launch_bounds__(256, DK == 128 ? 2 : 1) decode_split_mfma_kernel(const StepArgs sa) {
   __shared__ int32_t s_slot[kSlotTile];
   split_mfma_body<NEW, DK>(sa, s_slot, blockIdx.z, blockIdx.y, blockIdx.x);
+}
+
+// The split kernel with the new-token write and the rotary turn of q and
+// k_new (bf16, keys and values 128 wide).
+__global__ void __launch_bounds__(256, 2) decode_split_rope_kernel(const StepArgs sa) {
+  __shared__ int32_t s_slot[kSlotTile];
+  __shared__ __align__(16) float s_rope[kMfmaD];  // the table row of the new token
+  split_mfma_body<true, kMfmaD, true>(sa, s_slot, blockIdx.z, blockIdx.y, blockIdx.x, s_rope);
 }
 
 // ---------------------------------------------------------------------------
@@ -1107,6 +1168,16 @@ hipError_t launch_decode_split_store(const StepArgs &args, int head_dim, hipStre
     hipLaunchKernelGGL((decode_split_mfma_kernel<true, 192>), grid, dim3(256), 0, stream, sa);
   else
     hipLaunchKernelGGL((decode_split_mfma_kernel<true, 128>), grid, dim3(256), 0, stream, sa);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_split_rope(const StepArgs &args, hipStream_t stream) {
+  StepArgs sa = args;
+  DecodeArgs &a = sa.d;
+  a.n_chunks = (a.group + 15) / 16;
+  a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
+  const dim3 grid((a.n_kv_heads * a.n_chunks + 3) / 4, a.num_splits, a.batch);
+  hipLaunchKernelGGL(decode_split_rope_kernel, grid, dim3(256), 0, stream, sa);
   return hipGetLastError();
 }
 

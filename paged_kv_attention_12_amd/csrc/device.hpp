@@ -70,6 +70,22 @@ __device__ __forceinline__ int32_t slot_of_pos(const int32_t *row, uint32_t j, i
   return (int32_t)((page << page_shift) | (j & ((1u << page_shift) - 1u)));
 }
 
+// Rotary turn of one 16-byte piece of a bf16 row: pairs (a, b) = elements
+// (2j, 2j+1) times (c + i s) = (cs[2j], cs[2j+1]), in fp32, rounded to bf16.
+// The same arithmetic as the rotary kernel's, so a row turned here equals
+// the row that kernel writes, bit for bit.
+__device__ __forceinline__ uint4 rotate_bf16x8(const uint4 &w, const float *cs) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = bf16_lo(u[j]), b = bf16_hi(u[j]);
+    const float c = cs[2 * j], s = cs[2 * j + 1];
+    r[j] = pack_bf16x2(fmaf(a, c, -(b * s)), fmaf(a, s, b * c));
+  }
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 __device__ __forceinline__ uint4 load16(const void *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }

@@ -88,12 +88,21 @@ struct StepArgs {
   int32_t *sync;              // [batch * tasks] ticket counters, zero between calls
   void *out;                  // [batch, n_heads, head_dim] bf16
   int32_t tasks;              // kv-heads x head chunks (set by the launcher)
+  // Rotary embedding folded in (launch_decode_split_rope only): q and k_new
+  // arrive unrotated and are turned by row position_ids[b] of freqs.
+  const int32_t *position_ids;  // [batch]
+  const float *freqs;           // [max_pos, head_dim / 2, 2]: [cos, sin]
+  int64_t max_pos;
 };
 hipError_t launch_decode_step(const StepArgs &a, hipStream_t stream);
 // The split attention of one decode step with the new-token K/V write folded
 // in (bf16, head_dim 128); sync, out and tasks are not used.  The merge is a
 // separate launch.
 hipError_t launch_decode_split_store(const StepArgs &a, int head_dim, hipStream_t stream);
+// The same with the rotary embedding of q and k_new folded in (bf16, keys
+// and values 128 wide): every wavefront turns its query rows, and the new
+// key row is turned before it is attended and written.
+hipError_t launch_decode_split_rope(const StepArgs &a, hipStream_t stream);
 
 // Rotary embedding of the new tokens fused with their K/V write.
 struct RopeArgs {

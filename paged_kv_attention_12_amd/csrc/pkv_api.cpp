@@ -537,6 +537,66 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
                                 workspace, ws_bytes, out, stream);
 }
 
+pkv_status pkv_paged_decode_rope_store(const pkv_pool *pool, int32_t layer_id,
+                                       const pkv_step *step, const void *q, const void *k_new,
+                                       const void *v_new, const int32_t *position_ids,
+                                       const float *freqs_cis, int64_t max_pos, int32_t n_heads,
+                                       float sm_scale, int32_t num_splits, void *workspace,
+                                       size_t ws_bytes, void *out, void *stream) {
+  pkv_status st = check_pool(pool, layer_id);
+  if (st != PKV_OK) return st;
+  if (!step || !q || !workspace || !out) return PKV_ERR_NULL;
+  if (step->batch < 0 || n_heads <= 0 || n_heads % pool->n_kv_heads != 0 || num_splits <= 0 ||
+      num_splits > 65535 || step->batch > 65535 || max_pos <= 0)
+    return PKV_ERR_SHAPE;
+  if (!dims_ok(pool)) return PKV_ERR_UNSUPPORTED;
+  if (pool->dtype != PKV_BF16 || pool->head_dim != 128 || v_dim(pool) != 128 ||
+      n_heads / pool->n_kv_heads > 16)
+    return PKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(sm_scale)) return PKV_ERR_SHAPE;
+  if (step->batch == 0) return PKV_OK;
+  if (!k_new || !v_new || !step->out_cache_loc || !step->req_pool_indices || !step->seq_lens ||
+      !position_ids || !freqs_cis)
+    return PKV_ERR_NULL;
+  if (((uintptr_t)freqs_cis & 15u) != 0) return PKV_ERR_SHAPE;
+  if (step->n_new != step->batch) return PKV_ERR_SHAPE;  // one new token per request
+  if (step->max_len <= 0 || step->max_len > pool->max_ctx_len) return PKV_ERR_SHAPE;
+  if (ws_bytes < pkv_decode_workspace_bytes(step->batch, n_heads, v_dim(pool), num_splits))
+    return PKV_ERR_WORKSPACE_TOO_SMALL;
+  pkv::StepArgs sa{};
+  pkv::DecodeArgs &a = sa.d;
+  a.k_layer = k_layer_ptr(pool, layer_id);
+  a.v_layer = v_layer_ptr(pool, layer_id);
+  set_table(a, pool);
+  a.req_pool_indices = step->req_pool_indices;
+  a.seq_lens = step->seq_lens;
+  a.q = q;
+  a.o_part = reinterpret_cast<float *>(workspace);
+  a.ml_part = a.o_part + (size_t)step->batch * n_heads * num_splits * v_dim(pool);
+  a.batch = step->batch;
+  a.n_heads = n_heads;
+  a.n_kv_heads = pool->n_kv_heads;
+  a.group = n_heads / pool->n_kv_heads;
+  a.num_splits = num_splits;
+  a.chunk = decode_chunk(step->max_len, num_splits);
+  a.kv_start = nullptr;
+  a.split_stride = num_splits;
+  a.skip_empty = 1;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  sa.k_new = k_new;
+  sa.v_new = v_new;
+  sa.k_layer_w = const_cast<char *>(k_layer_ptr(pool, layer_id));
+  sa.v_layer_w = const_cast<char *>(v_layer_ptr(pool, layer_id));
+  sa.out_cache_loc = step->out_cache_loc;
+  sa.position_ids = position_ids;
+  sa.freqs = freqs_cis;
+  sa.max_pos = max_pos;
+  st = hip_status(pkv::launch_decode_split_rope(sa, (hipStream_t)stream));
+  if (st != PKV_OK) return st;
+  pkv::MergeArgs m = merge_args(a, out, nullptr, 0, 0);
+  return hip_status(pkv::launch_decode_merge(m, 1, v_dim(pool), (hipStream_t)stream));
+}
+
 pkv_status pkv_decode_prefix_groups(int32_t batch, const int32_t *req_pool_indices,
                                     const int32_t *seq_lens, const int32_t *req_to_token,
                                     int64_t num_reqs, int64_t max_ctx_len, int32_t page_size,

@@ -17,7 +17,11 @@ from tests.gpu_util import assert_close, say, to_np
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_captured_decode_loop_advances_metadata_in_place():
+@pytest.mark.parametrize("form", ["rope_then_step", "rope_in_step"])
+def test_graph_captured_decode_loop_advances_metadata_in_place(form):
+    """rope_then_step: the rotary write, then split attention and merge;
+    rope_in_step: the rotary turn folded into the split kernel
+    (pkv_paged_decode_rope_store), then the merge."""
     steps = 6
     start = np.array([300, 451, 17], dtype=np.int32)      # position of each request's first token
     H, Hk, d = 32, 8, 128
@@ -41,6 +45,11 @@ def test_graph_captured_decode_loop_advances_metadata_in_place():
     ws = api.decode_workspace(B_, H, d, ns)
 
     def one_step():
+        if form == "rope_in_step":
+            api.rope_decode_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, step, q,
+                                 k_new, v_new, freqs, case.sm_scale, num_splits=ns, workspace=ws,
+                                 out=out)
+            return
         api.rope_kv_store(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, step, q, k_new,
                           v_new, freqs, q_out=q_rot)
         api.decode_step(t["k_buffer"], t["v_buffer"], t["req_to_token"], 0, step, q_rot, None,
@@ -73,7 +82,7 @@ def test_graph_captured_decode_loop_advances_metadata_in_place():
         for x in (q, k_new, v_new):
             x.copy_(torch.randn(x.shape, generator=gen, device="cuda"))
         q0, kn0, vn0 = to_np(q), to_np(k_new), to_np(v_new)
-        say("graph loop step", k)
+        say("graph loop step", form, k)
         g.replay()
         torch.cuda.synchronize()
         pos = start + k
