@@ -302,6 +302,34 @@ def kernel_launch_spread(runner, launches=100, warm=False):
     return tuple(float(np.percentile(t, q)) for q in (10, 50, 90))
 
 
+def flushed_step_times(runner, n=20, flush_bytes=1 << 30, write=False):
+    """Per-step durations with the caches flushed first: before each step a
+    1 GiB device buffer (more than the L2s and the last-level cache hold) is
+    read by a sum, which leaves the caches holding clean lines of it, then a
+    HIP event pair on the step's stream brackets one step (successive
+    layers).  With write, the buffer is written instead: the step then also
+    pays for writing the flush's dirty lines back to HBM.  Returns (p10,
+    p50, p90) in seconds."""
+    torch = runner.torch
+    scratch = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda")
+    cur = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    runner.run_step(runner.layer_of(0))
+    for k, (a, b) in enumerate(ev):
+        if write:
+            scratch.fill_(k)
+        else:
+            scratch.sum()
+        a.record(cur)
+        runner.run_step(runner.layer_of(k))
+        b.record(cur)
+    torch.cuda.synchronize()
+    del scratch
+    t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    return tuple(float(np.percentile(t, q)) for q in (10, 50, 90))
+
+
 # ---------------------------------------------------------------------------
 # graph-captured decode loop: one token of a 32-layer forward per replay
 # ---------------------------------------------------------------------------
@@ -729,9 +757,11 @@ def main():
             r = head if L == L_head else StoredDecodeRunner(W.llama_b1_decode(L))
             spp, ok = timed_graph(r, 50, 5)
             kt_l = kernel_event_times(r, 32, reps=2)
+            fl = flushed_step_times(r)
             sweep[str(L)] = {"step_us": spp * 1e6, "split_kernel_us": float(kt_l.mean()) * 1e6,
                              "step_gbps": r.step_bytes() / spp / 1e9,
                              "split_kernel_gbps": r.kernel_bytes() / float(kt_l.mean()) / 1e9,
+                             "flushed_step_us_p10_p50_p90": [x * 1e6 for x in fl],
                              "num_splits": r.num_splits, "graph_ok": ok}
             if r is not head:
                 del r
@@ -748,7 +778,8 @@ def main():
             del rf
             torch.cuda.empty_cache()
             log(f"  B=1 L={L}: step {spp * 1e6:.1f} us (three launches {sp3 * 1e6:.1f} us, "
-                f"one launch {spf * 1e6:.1f} us), split kernel {kt_l.mean() * 1e6:.1f} us")
+                f"one launch {spf * 1e6:.1f} us), split kernel {kt_l.mean() * 1e6:.1f} us; "
+                f"caches flushed before each step: median {fl[1] * 1e6:.1f} us")
         extra["b1_decode_us"] = {L: v["step_us"] for L, v in sweep.items()}
         extra["b1_decode_three_launch_step_us"] = {L: v["three_launch_step_us"]
                                                    for L, v in sweep.items()}
