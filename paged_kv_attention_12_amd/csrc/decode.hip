@@ -257,16 +257,19 @@ __global__ void __launch_bounds__(256) decode_split_kernel(const DecodeArgs a) {
   }
 }
 
-// One workgroup per (request, head) row.  The splits are spread over
-// 256 / (D/4) split groups of D/4 threads (4 dims each).  Each thread loads
-// (m, l, o) of up to KB splits in one batch, the row maximum is reduced over
-// the workgroup, then every thread weighs what it holds: one memory round
-// trip for up to SG * KB splits.  Group sums are added through LDS.
-template <typename T, int D, int KB>
-__global__ void __launch_bounds__(256) decode_merge_kernel(const MergeArgs a) {
+// One workgroup of NT threads per (request, head) row.  The splits are
+// spread over NT / (D/4) split groups of D/4 threads (4 dims each).  Each
+// thread loads (m, l, o) of up to KB splits in one batch, the row maximum is
+// reduced over the workgroup, then every thread weighs what it holds: one
+// memory round trip for up to SG * KB splits.  Group sums are added through
+// LDS.
+template <typename T, int D, int KB, int NT>
+__global__ void __launch_bounds__(NT) decode_merge_kernel(const MergeArgs a) {
   constexpr int TPR = D / 4;
-  constexpr int SG = 256 / TPR;
-  __shared__ float s_red[4];
+  constexpr int SG = NT / TPR;
+  constexpr int NW = NT / 64;  // wavefronts
+  static_assert(NT % 64 == 0 && SG >= 1, "workgroup shape");
+  __shared__ float s_red[NW];
   __shared__ float4 s_num[SG][TPR];
   __shared__ float s_den[SG];
   const int r = blockIdx.x;
@@ -325,7 +328,9 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const MergeArgs a) {
     __syncthreads();  // s_red of the previous batch has been read
     if ((t & 63) == 0) s_red[t >> 6] = bm;
     __syncthreads();
-    const float Mn = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    float Mn = s_red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) Mn = fmaxf(Mn, s_red[w]);
     const float Mr = (Mn == kNegInf) ? 0.f : Mn;
     if (Mn != M && M != kNegInf) {  // earlier batches were weighed against M
       const float f = fast_exp2(M - Mr);
@@ -1098,16 +1103,18 @@ hipError_t decode_dispatch_ng(const DecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Few rows (a decode step of few requests): batches of 16 splits per thread,
-// one memory round trip for up to 128 splits of 128-dim rows.  Many rows:
-// batches of 8, whose registers (76 against 126) let half again as many
-// workgroups stay resident, for rows that mostly hold few splits.
+// Few rows (a decode step of few requests): 256 threads with batches of 16
+// splits per thread, one memory round trip for up to 128 splits of 128-dim
+// rows.  Many rows: 128 threads with batches of 12 (48 splits of 128-dim
+// rows per round trip), small enough that every row of a 2048-row step is
+// resident at once (a 256-thread workgroup per row left a third of them for
+// a second round).
 template <typename T, int D>
 void merge_d(const MergeArgs &a, hipStream_t stream) {
   if (a.rows > 1024)
-    hipLaunchKernelGGL((decode_merge_kernel<T, D, 8>), dim3(a.rows), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_merge_kernel<T, D, 12, 128>), dim3(a.rows), dim3(128), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_merge_kernel<T, D, 16>), dim3(a.rows), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_merge_kernel<T, D, 16, 256>), dim3(a.rows), dim3(256), 0, stream, a);
 }
 
 }  // namespace
