@@ -51,7 +51,7 @@ def log(*a):
 class DecodeRunner:
     """One decode workload on the device with its C-ABI arguments prebuilt."""
 
-    def __init__(self, case, fill_all_layers=True, num_splits=None):
+    def __init__(self, case, fill_all_layers=True, num_splits=None, load_policy=0):
         import torch
         import workloads as W
         from paged_kv_attention_12_amd import api, binding as B
@@ -75,7 +75,8 @@ class DecodeRunner:
         self.ws = api.decode_workspace(case.batch, H, d, self.num_splits)
         self.ws_bytes = self.ws.numel() * 4
         self.out = torch.empty_like(t["q"])
-        self.pool = B.make_pool(t["k_buffer"], t["v_buffer"], t["req_to_token"], case.page_size)
+        self.pool = B.make_pool(t["k_buffer"], t["v_buffer"], t["req_to_token"], case.page_size,
+                                load_policy)
         self.pool_ref = C.byref(self.pool)
         self.step_ref = C.byref(self.step.c)
         self.out_dtype = B.dtype_code(self.out)
@@ -739,7 +740,9 @@ def main():
                 "kernel": "decode_split_mfma_kernel", "bytes_per_launch": k_bytes,
                 "avg_launch_us": k_avg * 1e6, "launches": int(len(kt)) * args.kernel_launches,
                 "timing": "HIP events around a graph of back-to-back split-kernel launches",
-                "num_splits": head.num_splits}
+                "num_splits": head.num_splits,
+                "row_loads": ("non-temporal" if B.pkv_decode_load_kind(
+                    head.pool, 1, head.step.max_len) == 1 else "cached") + " (PKV_LOAD_AUTO)"}
     log(f"  step {sec_per_step * 1e6:.1f} us  {value:.0f} GB/s; split kernel {k_avg * 1e6:.1f} us "
         f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBPS:.1%})  graph_ok={graph_ok}")
     cold = kernel_launch_spread(head)
@@ -815,14 +818,17 @@ def main():
         torch.cuda.empty_cache()
 
         log("long-context decode")
-        rl = DecodeRunner(W.long_context_decode())
+        # its table is a permutation of the pool: no slot is shared between
+        # requests, so the rows are read once per step (PKV_LOAD_STREAM)
+        rl = DecodeRunner(W.long_context_decode(), load_policy=2)
         spp, ok = timed_graph(rl, 10, 2)
         ktl = kernel_event_times(rl, 4, reps=2)
         extra["long_context_decode"] = {
             "step_us": spp * 1e6, "split_kernel_us": float(ktl.mean()) * 1e6,
             "gbps": rl.kernel_bytes() / float(ktl.mean()) / 1e9,
             "frac_of_hbm_peak": rl.kernel_bytes() / float(ktl.mean()) / 1e9 / HBM_PEAK_GBPS,
-            "num_splits": rl.num_splits, "graph_ok": ok}
+            "num_splits": rl.num_splits, "graph_ok": ok,
+            "row_loads": "non-temporal (PKV_LOAD_STREAM: no slot shared between requests)"}
         if not args.no_cpu_baseline:
             log("cpu oracle baseline: long-context decode sample")
             cpu_long = cpu_baseline_long_context(rl)

@@ -62,6 +62,23 @@ typedef enum {
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 
+/* How the bf16 matrix-core decode kernels read K/V rows (pkv_pool.load_policy).
+ * The same section's allocator and prefix cache let requests share prompt
+ * slots; rows that another request of the step (or the next layer pass)
+ * reads again are worth keeping in the caches, rows read once are not.
+ *   PKV_LOAD_AUTO    (0) non-temporal row loads for a decode step of one
+ *                        request whose K/V over all n_layers of the pool
+ *                        exceed the 256 MiB last-level cache (nothing of it
+ *                        survives until it is read again); cached loads
+ *                        otherwise.  See pkv_decode_load_kind.
+ *   PKV_LOAD_CACHED  (1) always cached loads.
+ *   PKV_LOAD_STREAM  (2) always non-temporal row loads: for callers whose
+ *                        allocator never gives two requests the same slot.
+ * Affects speed only: results are the same bits under every policy.  The
+ * shared-prefix step, the one-launch step and the vector kernels (fp32,
+ * head_dim 64) always use cached loads. */
+typedef enum { PKV_LOAD_AUTO = 0, PKV_LOAD_CACHED = 1, PKV_LOAD_STREAM = 2 } pkv_load_policy;
+
 /* KVStorage + ReqToTokenPool ("Inference" guide, section "KVCache System").
  *
  * Pages.  The same section runs the pool in paged mode with page_size 1 or
@@ -96,6 +113,7 @@ typedef struct {
                                    qk_rope_head_dim = head_dim dims and values of
                                    v_head_dim: v_buffer is then
                                    [n_layers, size, n_kv_heads, v_head_dim]      */
+  int32_t load_policy;          /* pkv_load_policy; 0 (zeroed struct): AUTO      */
 } pkv_pool;
 
 /* One step's KVCache metadata (same section).  Arrays are device pointers;
@@ -256,6 +274,14 @@ size_t pkv_decode_workspace_bytes(int32_t max_batch, int32_t n_heads, int32_t he
  * device balances the load; clamped to [1, max_splits]. */
 int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_heads,
                                int32_t max_len, int64_t total_len, int32_t max_splits);
+
+/* Host, no device access: whether the bf16 matrix-core decode kernels
+ * (pkv_paged_decode, pkv_paged_decode_store, pkv_paged_decode_rope_store)
+ * read K/V rows with non-temporal loads for a decode step of `batch`
+ * requests with max_len as pkv_step.max_len on this pool, under its
+ * load_policy (see pkv_load_policy): 1 non-temporal, 0 cached, -1 for a null
+ * pool or invalid fields.  Affects speed only. */
+int32_t pkv_decode_load_kind(const pkv_pool *pool, int32_t batch, int32_t max_len);
 
 /* ------------------------------------------------------------------------
  * Split-KV paged decode ("Inference" guide, section "KV Cache": the single

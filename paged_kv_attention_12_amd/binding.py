@@ -30,6 +30,10 @@ PKV_ERR_SCRATCH_LIMIT = 8
 PKV_F32 = 0
 PKV_BF16 = 1
 
+PKV_LOAD_AUTO = 0
+PKV_LOAD_CACHED = 1
+PKV_LOAD_STREAM = 2
+
 EXPORTED = (
     "pkv_status_string", "pkv_last_hip_error", "pkv_build_step", "pkv_validate_step",
     "pkv_kv_store", "pkv_decode_workspace_bytes", "pkv_decode_pick_splits",
@@ -37,7 +41,7 @@ EXPORTED = (
     "pkv_paged_decode_step", "pkv_decode_step_pick_splits", "pkv_paged_decode_store",
     "pkv_build_positions", "pkv_rope_kv_store", "pkv_decode_advance", "pkv_prefill_blocks",
     "pkv_paged_decode_store_noalloc", "pkv_decode_prefix_groups", "pkv_paged_decode_shared",
-    "pkv_rope_kv_store_partial", "pkv_paged_decode_rope_store",
+    "pkv_rope_kv_store_partial", "pkv_paged_decode_rope_store", "pkv_decode_load_kind",
 )
 
 PKV_PREFIX_GROUP_MAX = 16
@@ -56,6 +60,7 @@ class pkv_pool(C.Structure):
         ("n_layers", C.c_int64), ("size", C.c_int64), ("num_reqs", C.c_int64),
         ("max_ctx_len", C.c_int64), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
         ("dtype", C.c_int32), ("page_size", C.c_int32), ("v_head_dim", C.c_int32),
+        ("load_policy", C.c_int32),
     ]
 
 
@@ -106,6 +111,7 @@ def load() -> C.CDLL:
         "pkv_kv_store": (C.c_int, [C.POINTER(pkv_pool), i32, P, P, P, i64, P]),
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "pkv_decode_pick_splits": (i32, [i32, i32, i32, i32, i64, i32]),
+        "pkv_decode_load_kind": (i32, [C.POINTER(pkv_pool), i32, i32]),
         "pkv_paged_decode": (C.c_int, [C.POINTER(pkv_pool), i32, C.POINTER(pkv_step), P, i32,
                                        f32, i32, P, sz, P]),
         "pkv_paged_decode_merge": (C.c_int, [i32, i32, i32, C.c_int, i32, P, sz, P, P]),
@@ -219,11 +225,13 @@ def _check_new(k_new, v_new, k_buffer, v_buffer, rows: int) -> None:
                          "the pool dtype")
 
 
-def make_pool(k_buffer, v_buffer, req_to_token, page_size: int = 1) -> pkv_pool:
+def make_pool(k_buffer, v_buffer, req_to_token, page_size: int = 1,
+              load_policy: int = PKV_LOAD_AUTO) -> pkv_pool:
     """pkv_pool view of device tensors k_buffer / v_buffer [n_layers, size,
     n_kv_heads, head_dim] and req_to_token int32 [num_reqs, entries]: slots
     (page_size 1, max_ctx_len = entries) or physical page ids of pages of
-    page_size tokens (max_ctx_len = entries * page_size)."""
+    page_size tokens (max_ctx_len = entries * page_size).  load_policy: how
+    the decode kernels read K/V rows (PKV_LOAD_*)."""
     import torch
     if k_buffer.shape[:3] != v_buffer.shape[:3] or k_buffer.dtype != v_buffer.dtype:
         raise ValueError("k_buffer and v_buffer differ in layers, slots, heads or dtype")
@@ -239,6 +247,7 @@ def make_pool(k_buffer, v_buffer, req_to_token, page_size: int = 1) -> pkv_pool:
     p.max_ctx_len = int(req_to_token.shape[1]) * max(int(page_size), 1)
     p.page_size = int(page_size)
     p.dtype = dtype_code(k_buffer)
+    p.load_policy = int(load_policy)
     return p
 
 
@@ -371,6 +380,12 @@ def pkv_decode_workspace_bytes(max_batch: int, n_heads: int, head_dim: int,
     return int(load().pkv_decode_workspace_bytes(max_batch, n_heads, head_dim, num_splits))
 
 
+def pkv_decode_load_kind(pool: pkv_pool, batch: int, max_len: int) -> int:
+    """1 if the decode kernels read this step's K/V rows with non-temporal
+    loads under pool.load_policy, 0 if cached, -1 for invalid fields."""
+    return int(load().pkv_decode_load_kind(C.byref(pool), int(batch), int(max_len)))
+
+
 def pkv_decode_pick_splits(batch: int, n_kv_heads: int, n_heads: int, max_len: int,
                            total_len: int = 0, max_splits: int = 1024) -> int:
     return int(load().pkv_decode_pick_splits(batch, n_kv_heads, n_heads, max_len,
@@ -378,8 +393,9 @@ def pkv_decode_pick_splits(batch: int, n_kv_heads: int, n_heads: int, max_len: i
 
 
 def pkv_paged_decode(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,
-                     sm_scale: float, num_splits: int, workspace, page_size: int = 1) -> None:
-    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
+                     sm_scale: float, num_splits: int, workspace, page_size: int = 1,
+                     load_policy: int = PKV_LOAD_AUTO) -> None:
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size, load_policy)
     if q.dim() != 3 or q.shape[0] != step.batch or q.shape[2] != k_buffer.shape[3] \
             or q.dtype != k_buffer.dtype:
         raise ValueError("q must be [batch, n_heads, head_dim] in the pool dtype")
@@ -424,8 +440,9 @@ def pkv_paged_decode_step(k_buffer, v_buffer, req_to_token, layer_id: int, step:
 
 def pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id: int, step: pkv_step, q,
                            k_new, v_new, sm_scale: float, num_splits: int, workspace,
-                           out, page_size: int = 1) -> None:
-    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
+                           out, page_size: int = 1,
+                           load_policy: int = PKV_LOAD_AUTO) -> None:
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size, load_policy)
     _check_q_out(q, out, k_buffer, v_buffer, step.batch)
     _check_new(k_new, v_new, k_buffer, v_buffer, step.batch)
     st = load().pkv_paged_decode_store(
@@ -439,11 +456,12 @@ def pkv_paged_decode_store(k_buffer, v_buffer, req_to_token, layer_id: int, step
 def pkv_paged_decode_rope_store(k_buffer, v_buffer, req_to_token, layer_id: int,
                                 step: pkv_step, q, k_new, v_new, position_ids, freqs_cis,
                                 sm_scale: float, num_splits: int, workspace, out,
-                                page_size: int = 1) -> None:
+                                page_size: int = 1,
+                                load_policy: int = PKV_LOAD_AUTO) -> None:
     """The two-launch decode step with the rotary turn of q and k_new folded
     in (pkv_paged_decode_rope_store)."""
     import torch
-    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size)
+    pool = make_pool(k_buffer, v_buffer, req_to_token, page_size, load_policy)
     _check_q_out(q, out, k_buffer, v_buffer, step.batch)
     _check_new(k_new, v_new, k_buffer, v_buffer, step.batch)
     if freqs_cis.dim() != 3 or tuple(freqs_cis.shape[1:]) != (int(k_buffer.shape[3]) // 2, 2) \

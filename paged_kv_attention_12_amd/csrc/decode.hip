@@ -419,10 +419,11 @@ constexpr int kKT = 32;      // keys per iteration of a wavefront
 // with seq_lens so that the two loads share one memory round trip).  qcol is
 // the query row of this lane's column (a query head of one request), or null
 // for an unused column.  Runs of staged slot ids hold a.chunk keys (at most
-// kSlotTile).  On return o[e][i] holds the
+// kSlotTile).  With STREAM the K/V rows are read with non-temporal loads.
+// On return o[e][i] holds the
 // unnormalised O[column c][32g + 8i + e] against the base-2 running max m_run,
 // and l_tot the running sum (both per column, equal in the four lane groups).
-template <int TS, bool NEW, int P, int DK = kMfmaD, bool ROPE = false>
+template <int TS, bool NEW, int P, int DK = kMfmaD, bool ROPE = false, bool STREAM = false>
 __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot, int pool_row,
                                             int start, int end, int first, bool active, int hk,
                                             const uint16_t *qcol, const uint16_t *knew,
@@ -492,6 +493,12 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
   // of the round read the round's last row instead (finite data whose score is
   // masked to -inf, so its weight is 0): the loads stay unconditional, which
   // lets the compiler keep several tiles in flight.
+  auto row16 = [](const uint16_t *p) {
+    if constexpr (STREAM)
+      return load16_nt(p);
+    else
+      return load16(p);
+  };
   auto fetch = [&](uint4(&kx)[2][KS], uint4(&vx)[8], int j0, int r0, int r1) {
     const int last = r1 - 1 - r0;
     const int jb = j0 - r0;
@@ -505,13 +512,13 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
       const uint16_t *kp = kbase + (int64_t)s_slot[jk[t]] * krow_elems;
       if constexpr (NEW) kp = (r0 + jk[t] == newpos) ? knew_l : kp;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) kx[t][k] = load16(kp + 32 * k);
+      for (int k = 0; k < KS; ++k) kx[t][k] = row16(kp + 32 * k);
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const uint16_t *vp = vbase + (int64_t)s_slot[jv[x]] * vrow_elems;
       if constexpr (NEW) vp = (r0 + jv[x] == newpos) ? vnew_l : vp;
-      vx[x] = load16(vp);
+      vx[x] = row16(vp);
     }
   };
 
@@ -643,7 +650,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs &a, int32_t *s_slot
 // the split reads them as pool rows (one wavefront per kv-head: at most 16
 // query heads per kv-head, and out_cache_loc[b] the slot of position
 // seq_lens[b] - 1).
-template <bool NEW, int DK = kMfmaD, bool ROPE = false>
+template <bool NEW, int DK = kMfmaD, bool ROPE = false, bool STREAM = false>
 __device__ __forceinline__ void split_mfma_body(const StepArgs &sa, int32_t *s_slot, int b, int s,
                                                 int wx, float *s_rope = nullptr) {
   constexpr int D = kMfmaD;  // value width; keys are DK wide
@@ -735,15 +742,17 @@ __device__ __forceinline__ void split_mfma_body(const StepArgs &sa, int32_t *s_s
   if constexpr (ROPE) {
     // The new rows go to the pool first (turned key, value), then every
     // split reads pool rows only.
-    attend_mfma<1, false, kRing, DK, true>(a, s_slot, pool_row, start, end, 0, active, hk, qcol,
+    attend_mfma<1, false, kRing, DK, true, STREAM>(a, s_slot, pool_row, start, end, 0, active, hk, qcol,
                                            nullptr, nullptr, -1, o, m_run, l_tot, rope_row,
                                            s_rope, writer ? new_dst : nullptr, new_piece);
   } else if (NEW && start <= newpos && newpos < end) {
-    attend_mfma<1, true, kRing, DK>(a, s_slot, pool_row, start, end, 0, active, hk, qcol, knew,
+    attend_mfma<1, true, kRing, DK, false, STREAM>(a, s_slot, pool_row, start, end, 0, active, hk,
+                                                   qcol, knew,
                                     vnew, newpos, o, m_run, l_tot);
   } else {
-    attend_mfma<1, false, kRing, DK>(a, s_slot, pool_row, start, end, 0, active, hk, qcol,
-                                     nullptr, nullptr, -1, o, m_run, l_tot);
+    attend_mfma<1, false, kRing, DK, false, STREAM>(a, s_slot, pool_row, start, end, 0, active,
+                                                    hk, qcol, nullptr, nullptr, -1, o, m_run,
+                                                    l_tot);
   }
   if (NEW && !ROPE && writer) store16(new_dst, new_piece);
   if (!active || !col_ok) return;
@@ -763,18 +772,20 @@ __device__ __forceinline__ void split_mfma_body(const StepArgs &sa, int32_t *s_s
 
 // Keys 192 wide (MLA-shaped layers) hold more registers per wavefront: one
 // wavefront per SIMD, instead of two for 128-wide keys.
-template <bool NEW, int DK>
+template <bool NEW, int DK, bool STREAM>
 __global__ void __launch_bounds__(256, DK == 128 ? 2 : 1) decode_split_mfma_kernel(const StepArgs sa) {
   __shared__ int32_t s_slot[kSlotTile];
-  split_mfma_body<NEW, DK>(sa, s_slot, blockIdx.z, blockIdx.y, blockIdx.x);
+  split_mfma_body<NEW, DK, false, STREAM>(sa, s_slot, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
 // The split kernel with the new-token write and the rotary turn of q and
 // k_new (bf16, keys and values 128 wide).
+template <bool STREAM>
 __global__ void __launch_bounds__(256, 2) decode_split_rope_kernel(const StepArgs sa) {
   __shared__ int32_t s_slot[kSlotTile];
   __shared__ __align__(16) float s_rope[kMfmaD];  // the table row of the new token
-  split_mfma_body<true, kMfmaD, true>(sa, s_slot, blockIdx.z, blockIdx.y, blockIdx.x, s_rope);
+  split_mfma_body<true, kMfmaD, true, STREAM>(sa, s_slot, blockIdx.z, blockIdx.y, blockIdx.x,
+                                              s_rope);
 }
 
 // ---------------------------------------------------------------------------
@@ -1123,6 +1134,20 @@ bool decode_mfma_shape(int dtype, int head_dim, int v_head_dim) {
   return dtype == 1 && v_head_dim == kMfmaD && (head_dim == 128 || head_dim == 192);
 }
 
+// The matrix-core split kernel for the key width and load kind of sa.
+template <bool NEW>
+void split_d(const StepArgs &sa, int head_dim, dim3 grid, hipStream_t stream) {
+  const bool st = sa.d.stream_rows != 0;
+  if (head_dim == 192 && st)
+    hipLaunchKernelGGL((decode_split_mfma_kernel<NEW, 192, true>), grid, dim3(256), 0, stream, sa);
+  else if (head_dim == 192)
+    hipLaunchKernelGGL((decode_split_mfma_kernel<NEW, 192, false>), grid, dim3(256), 0, stream, sa);
+  else if (st)
+    hipLaunchKernelGGL((decode_split_mfma_kernel<NEW, 128, true>), grid, dim3(256), 0, stream, sa);
+  else
+    hipLaunchKernelGGL((decode_split_mfma_kernel<NEW, 128, false>), grid, dim3(256), 0, stream, sa);
+}
+
 hipError_t launch_paged_decode(const DecodeArgs &args, int dtype, int head_dim, int v_head_dim,
                                hipStream_t stream) {
   DecodeArgs a = args;
@@ -1137,10 +1162,7 @@ hipError_t launch_paged_decode(const DecodeArgs &args, int dtype, int head_dim, 
     StepArgs sa{};
     sa.d = a;
     const dim3 grid((a.n_kv_heads * a.n_chunks + 3) / 4, a.num_splits, a.batch);
-    if (head_dim == 192)
-      hipLaunchKernelGGL((decode_split_mfma_kernel<false, 192>), grid, dim3(256), 0, stream, sa);
-    else
-      hipLaunchKernelGGL((decode_split_mfma_kernel<false, 128>), grid, dim3(256), 0, stream, sa);
+    split_d<false>(sa, head_dim, grid, stream);
     return hipGetLastError();
   }
   if (head_dim != v_head_dim) return hipErrorInvalidValue;
@@ -1171,10 +1193,7 @@ hipError_t launch_decode_split_store(const StepArgs &args, int head_dim, hipStre
   a.n_chunks = (a.group + 15) / 16;
   a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
   const dim3 grid((a.n_kv_heads * a.n_chunks + 3) / 4, a.num_splits, a.batch);
-  if (head_dim == 192)
-    hipLaunchKernelGGL((decode_split_mfma_kernel<true, 192>), grid, dim3(256), 0, stream, sa);
-  else
-    hipLaunchKernelGGL((decode_split_mfma_kernel<true, 128>), grid, dim3(256), 0, stream, sa);
+  split_d<true>(sa, head_dim, grid, stream);
   return hipGetLastError();
 }
 
@@ -1184,7 +1203,10 @@ hipError_t launch_decode_split_rope(const StepArgs &args, hipStream_t stream) {
   a.n_chunks = (a.group + 15) / 16;
   a.heads_per_chunk = (a.group + a.n_chunks - 1) / a.n_chunks;
   const dim3 grid((a.n_kv_heads * a.n_chunks + 3) / 4, a.num_splits, a.batch);
-  hipLaunchKernelGGL(decode_split_rope_kernel, grid, dim3(256), 0, stream, sa);
+  if (a.stream_rows)
+    hipLaunchKernelGGL(decode_split_rope_kernel<true>, grid, dim3(256), 0, stream, sa);
+  else
+    hipLaunchKernelGGL(decode_split_rope_kernel<false>, grid, dim3(256), 0, stream, sa);
   return hipGetLastError();
 }
 

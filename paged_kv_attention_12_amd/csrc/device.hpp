@@ -89,6 +89,13 @@ __device__ __forceinline__ uint4 rotate_bf16x8(const uint4 &w, const float *cs) 
 __device__ __forceinline__ uint4 load16(const void *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }
+// A 16-byte load with the non-temporal hint (global_load_dwordx4 ... nt):
+// for rows read once, so that they do not displace lines read again.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ void store16(void *p, uint4 v) {
   *reinterpret_cast<uint4 *>(p) = v;
 }

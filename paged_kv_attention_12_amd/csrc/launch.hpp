@@ -68,6 +68,8 @@ struct DecodeArgs {
   // Splits with no keys leave their partial unwritten (the merge is told
   // which splits hold keys); 0: every split writes one.
   int32_t skip_empty;
+  // Matrix-core split kernels: K/V rows read with non-temporal loads.
+  int32_t stream_rows;
 };
 // dtype: 0 = f32, 1 = bf16.  head_dim: key width; v_head_dim: value width.
 hipError_t launch_paged_decode(const DecodeArgs &a, int dtype, int head_dim, int v_head_dim,

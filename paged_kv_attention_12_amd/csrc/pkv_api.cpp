@@ -63,7 +63,22 @@ pkv_status check_pool(const pkv_pool *p, int32_t layer_id) {
   const int sh = page_shift_of(p->page_size);
   if (sh < 0 || p->size % (int64_t(1) << sh) != 0) return PKV_ERR_SHAPE;
   if (layer_id < 0 || layer_id >= p->n_layers) return PKV_ERR_SHAPE;
+  if (p->load_policy < PKV_LOAD_AUTO || p->load_policy > PKV_LOAD_STREAM) return PKV_ERR_SHAPE;
   return PKV_OK;
+}
+
+// MI355X's last-level (Infinity) cache.
+constexpr int64_t kLastLevelCacheBytes = int64_t(256) << 20;
+
+// Whether the matrix-core decode kernels read K/V rows with non-temporal
+// loads for a step of `batch` requests of at most max_len keys
+// (pkv_load_policy).
+bool stream_rows(const pkv_pool *p, int32_t batch, int32_t max_len) {
+  if (p->load_policy == PKV_LOAD_STREAM) return true;
+  if (p->load_policy == PKV_LOAD_CACHED) return false;
+  const int64_t row = (int64_t)p->n_kv_heads * (p->head_dim + v_dim(p)) *
+                      (int64_t)dtype_bytes(p->dtype);
+  return batch == 1 && p->n_layers * (int64_t)max_len * row > kLastLevelCacheBytes;
 }
 
 // The table fields every gathering kernel takes.
@@ -398,9 +413,18 @@ pkv_status pkv_paged_decode(const pkv_pool *pool, int32_t layer_id, const pkv_st
   a.kv_start = nullptr;
   a.split_stride = num_splits;
   a.skip_empty = 0;
+  a.stream_rows = stream_rows(pool, step->batch, step->max_len);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   return hip_status(pkv::launch_paged_decode(a, pool->dtype == PKV_BF16 ? 1 : 0,
                                               pool->head_dim, v_dim(pool), (hipStream_t)stream));
+}
+
+int32_t pkv_decode_load_kind(const pkv_pool *pool, int32_t batch, int32_t max_len) {
+  if (!pool || batch < 0 || max_len < 0 || pool->n_layers <= 0 || pool->n_kv_heads <= 0 ||
+      pool->head_dim <= 0 || pool->v_head_dim < 0 || !dtype_ok(pool->dtype) ||
+      pool->load_policy < PKV_LOAD_AUTO || pool->load_policy > PKV_LOAD_STREAM)
+    return -1;
+  return stream_rows(pool, batch, max_len) ? 1 : 0;
 }
 
 int32_t pkv_decode_step_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_heads,
@@ -528,6 +552,7 @@ pkv_status pkv_paged_decode_store(const pkv_pool *pool, int32_t layer_id, const 
     // Splits past a request's keys leave no partial; the merge reads only the
     // ones that hold keys.
     a.skip_empty = 1;
+    a.stream_rows = stream_rows(pool, step->batch, step->max_len);
     st = hip_status(pkv::launch_decode_split_store(sa, pool->head_dim, (hipStream_t)stream));
     if (st != PKV_OK) return st;
     pkv::MergeArgs m = merge_args(a, out, nullptr, 0, 0);
@@ -591,6 +616,7 @@ pkv_status pkv_paged_decode_rope_store(const pkv_pool *pool, int32_t layer_id,
   sa.position_ids = position_ids;
   sa.freqs = freqs_cis;
   sa.max_pos = max_pos;
+  a.stream_rows = stream_rows(pool, step->batch, step->max_len);
   st = hip_status(pkv::launch_decode_split_rope(sa, (hipStream_t)stream));
   if (st != PKV_OK) return st;
   pkv::MergeArgs m = merge_args(a, out, nullptr, 0, 0);

@@ -3,7 +3,9 @@
  * checks the step metadata of two small steps (one-token pages and 4-token
  * pages) against values worked out by hand, plus the checked mode.  Prints
  * "ok" and exits 0 on success. */
+#include <stddef.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "pkv.h"
@@ -13,7 +15,7 @@ static int expect(int cond, const char *what) {
   return cond ? 0 : 1;
 }
 
-int main(void) {
+int main(int argc, char **argv) {
   int bad = 0;
   /* one-token pages: rows 2, 0, 1 with 3, 5, 2 tokens, 1, 2, 2 of them new */
   const int32_t table[3 * 6] = {10, 11, 12, 13, 14, 15, 20, 21, 22, 23, 24, 25,
@@ -50,6 +52,33 @@ int main(void) {
                 "workspace bytes");
   bad |= expect(strcmp(pkv_status_string(PKV_ERR_WORKSPACE_TOO_SMALL), "workspace too small") == 0,
                 "status string");
+  /* Load policy: a zeroed pool field is PKV_LOAD_AUTO, which streams a
+   * one-request step whose K/V over all layers exceed 256 MiB. */
+  pkv_pool pool;
+  memset(&pool, 0, sizeof pool);
+  pool.k_buffer = pool.v_buffer = (void *)0x1000;
+  pool.req_to_token = (const int32_t *)0x2000;
+  pool.n_layers = 32;
+  pool.size = 65536;
+  pool.num_reqs = 1;
+  pool.max_ctx_len = 32768;
+  pool.n_kv_heads = 8;
+  pool.head_dim = 128;
+  pool.dtype = PKV_BF16;
+  bad |= expect(pkv_decode_load_kind(&pool, 1, 32768) == 1, "auto: one long request streams");
+  bad |= expect(pkv_decode_load_kind(&pool, 1, 1024) == 0, "auto: short request cached");
+  bad |= expect(pkv_decode_load_kind(&pool, 2, 32768) == 0, "auto: batches cached");
+  pool.load_policy = PKV_LOAD_STREAM;
+  bad |= expect(pkv_decode_load_kind(&pool, 64, 16) == 1, "stream policy");
+
+  /* The ctypes binding's layout (sizes and the offset of the last pool
+   * field, passed by the test) matches the compiler's. */
+  if (argc == 4) {
+    bad |= expect(sizeof(pkv_pool) == (size_t)atol(argv[1]), "sizeof pkv_pool");
+    bad |= expect(offsetof(pkv_pool, load_policy) == (size_t)atol(argv[2]),
+                  "offset of pkv_pool.load_policy");
+    bad |= expect(sizeof(pkv_step) == (size_t)atol(argv[3]), "sizeof pkv_step");
+  }
   if (!bad) printf("ok\n");
   return bad;
 }

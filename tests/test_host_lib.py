@@ -223,6 +223,39 @@ def test_argument_errors_before_launch(lib):
                                      None) == B.PKV_ERR_SHAPE
 
 
+def test_decode_load_kind(lib):
+    """pkv_pool.load_policy: AUTO streams a one-request step whose K/V over
+    all layers exceed the 256 MiB last-level cache; CACHED and STREAM
+    override; invalid fields give -1 and entry points refuse them."""
+    p = _fake_pool(n_layers=32)
+    p.n_kv_heads = 8                     # rows of 8 * (128 + 128) * 2 = 4096 bytes
+    assert p.load_policy == B.PKV_LOAD_AUTO
+    # 32 layers * L * 4096 bytes against 256 MiB: the boundary is L = 2048
+    assert B.pkv_decode_load_kind(p, 1, 2048) == 0
+    assert B.pkv_decode_load_kind(p, 1, 2049) == 1
+    assert B.pkv_decode_load_kind(p, 1, 32768) == 1
+    assert B.pkv_decode_load_kind(p, 1, 1024) == 0
+    for batch in (0, 2, 8, 64):        # requests may share slots: cached
+        assert B.pkv_decode_load_kind(p, batch, 131072) == 0
+    one = _fake_pool(n_layers=1)
+    one.n_kv_heads = 8
+    assert B.pkv_decode_load_kind(one, 1, 32768) == 0   # 134 MB fit the cache
+    mla = _fake_pool(head_dim=192, n_layers=32)
+    mla.v_head_dim, mla.n_kv_heads = 128, 8           # rows of 8 * 320 * 2 bytes
+    assert B.pkv_decode_load_kind(mla, 1, 1638) == 0  # 32 * 1638 * 5120 < 2^28
+    assert B.pkv_decode_load_kind(mla, 1, 1639) == 1
+    p.load_policy = B.PKV_LOAD_CACHED
+    assert B.pkv_decode_load_kind(p, 1, 131072) == 0
+    p.load_policy = B.PKV_LOAD_STREAM
+    assert B.pkv_decode_load_kind(p, 64, 16) == 1
+    for bad in (-1, 3):
+        p.load_policy = bad
+        assert B.pkv_decode_load_kind(p, 1, 32768) == -1
+        fake = C.c_void_p(0x4000)
+        assert lib.pkv_kv_store(C.byref(p), 0, fake, fake, fake, 4, None) == B.PKV_ERR_SHAPE
+    assert lib.pkv_decode_load_kind(None, 1, 32768) == -1
+
+
 def test_fused_step_split_choice(lib):
     # a quarter of the single-wave choice (four waves share a split), at least 1
     for args in [(1, 8, 32, 1024, 1024), (1, 8, 32, 32768, 32768), (8, 8, 64, 131072, 8 * 131072),
@@ -437,7 +470,9 @@ def test_c_caller_of_the_header(lib, tmp_path):
     src = os.path.join(ROOT, "tests", "c", "host_abi.c")
     subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
                     src, "-L", libdir, "-lpkv", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
-    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    layout = [str(C.sizeof(B.pkv_pool)), str(B.pkv_pool.load_policy.offset),
+              str(C.sizeof(B.pkv_step))]
+    r = subprocess.run([exe, *layout], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
 
 
