@@ -87,7 +87,10 @@ __device__ __forceinline__ uint4 rotate(const uint4 &w, const float *f) {
 // Consecutive threads cover consecutive pieces of a row, so every row is one
 // coalesced run.  Positions outside [0, max_pos) read the nearest table row
 // (the caller guarantees valid positions; the clamp only keeps reads in
-// bounds).
+// bounds).  q, k_new and v_new are read once, with non-temporal loads, so
+// that they do not displace the table rows every head row of a token reads
+// (4% faster on a 20356-token step than cached loads; non-temporal stores
+// measured no faster).
 template <typename T>
 __global__ void __launch_bounds__(256) rope_kv_store_kernel(const RopeArgs a, int64_t q_pieces,
                                                             int64_t kv_pieces) {
@@ -99,7 +102,7 @@ __global__ void __launch_bounds__(256) rope_kv_store_kernel(const RopeArgs a, in
   if (t < q_pieces) {
     const int64_t row = t / ppr;
     const int c = (int)(t - row * ppr);
-    const uint4 w = reinterpret_cast<const uint4 *>(a.q)[t];
+    const uint4 w = load16_nt(reinterpret_cast<const uint4 *>(a.q) + t);
     uint4 r = w;
     if (c >= first_rot) {
       const int64_t i = row / a.n_heads;
@@ -114,7 +117,7 @@ __global__ void __launch_bounds__(256) rope_kv_store_kernel(const RopeArgs a, in
     const int64_t i = row / a.n_kv_heads;
     const int64_t hk = row - i * a.n_kv_heads;
     const int64_t loc = a.out_cache_loc[i];
-    const uint4 kw = reinterpret_cast<const uint4 *>(a.k_new)[u];
+    const uint4 kw = load16_nt(reinterpret_cast<const uint4 *>(a.k_new) + u);
     uint4 kr = kw;
     if (c >= first_rot) {
       const int64_t p = min(max((int64_t)a.position_ids[i], (int64_t)0), a.max_pos - 1);
@@ -122,7 +125,7 @@ __global__ void __launch_bounds__(256) rope_kv_store_kernel(const RopeArgs a, in
     }
     reinterpret_cast<uint4 *>(a.k_layer)[(loc * a.n_kv_heads + hk) * ppr + c] = kr;
     if (c < vppr) {
-      const uint4 vw = reinterpret_cast<const uint4 *>(a.v_new)[row * vppr + c];
+      const uint4 vw = load16_nt(reinterpret_cast<const uint4 *>(a.v_new) + row * vppr + c);
       reinterpret_cast<uint4 *>(a.v_layer)[(loc * a.n_kv_heads + hk) * vppr + c] = vw;
     }
   }
