@@ -349,12 +349,13 @@ int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_head
   // Wavefront-tokens of work: every (kv-head, head chunk) walks every token.
   const int64_t work = total_len * n_kv_heads * chunks;
   // Equal lengths: about 1024 long-running wavefronts (one per SIMD) keep the
-  // per-split start-up and merge cost low.  Ragged lengths: short splits of at
-  // most 256 tokens, about 8K of them (eight per SIMD), so that the device
-  // balances the load; twice as many measured slower (each split pays the
-  // start-up chain again).
+  // per-split start-up and merge cost low.  Ragged lengths: splits of at most
+  // 512 tokens, about 4K of them (four per SIMD), so that the device balances
+  // the load; twice as many measured 2-3% slower on a 64-request batch (each
+  // split pays the start-up chain again, and the merge reads more partials),
+  // and much longer splits leave the end of the launch to a few of them.
   const bool ragged = (int64_t)batch * max_len > total_len + total_len / 4;
-  int64_t chunk = ragged ? std::min<int64_t>(256, work / 8192)
+  int64_t chunk = ragged ? std::min<int64_t>(512, work / 4096)
                          : std::min<int64_t>(2048, work / 1024);
   chunk = std::max<int64_t>(chunk, 16);
   int64_t s = ((int64_t)max_len + chunk - 1) / chunk;

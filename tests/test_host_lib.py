@@ -147,9 +147,10 @@ def test_workspace_bytes_and_split_choice(lib):
     assert B.pkv_decode_pick_splits(1, 8, 32, 32768, 32768) == 128
     assert B.pkv_decode_pick_splits(1, 8, 32, 1024, 1024) == 64
     assert B.pkv_decode_pick_splits(8, 8, 64, 131072, 8 * 131072) == 64
-    # ragged: 32 splits of 256 tokens, one more: an odd count spreads a
-    # request's 2 x 33 workgroups over the most XCD offsets
-    assert B.pkv_decode_pick_splits(64, 8, 32, 8192, 266000) == 33
+    # ragged: 266000 * 8 / 4096 = 519 wavefront-tokens, capped at 512 tokens
+    # per split: 16 splits, one more: an odd count spreads a request's
+    # 2 x 17 workgroups over the most XCD offsets
+    assert B.pkv_decode_pick_splits(64, 8, 32, 8192, 266000) == 17
     rng = np.random.default_rng(5)
     for _ in range(200):
         batch = int(rng.integers(2, 200))
