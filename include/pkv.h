@@ -270,8 +270,9 @@ size_t pkv_decode_workspace_bytes(int32_t max_batch, int32_t n_heads, int32_t he
  * batch, head counts, the host max_len and the step's total context tokens
  * (kv_indptr[batch]; <= 0 means batch * max_len) it picks num_splits for
  * pkv_paged_decode: for equal lengths about one long-running wavefront per
- * SIMD, for ragged lengths many short splits (at most 256 tokens) so the
- * device balances the load; clamped to [1, max_splits]. */
+ * SIMD, for ragged lengths about four splits per SIMD of at most 512 tokens
+ * (an odd count) so the device balances the load; clamped to
+ * [1, max_splits]. */
 int32_t pkv_decode_pick_splits(int32_t batch, int32_t n_kv_heads, int32_t n_heads,
                                int32_t max_len, int64_t total_len, int32_t max_splits);
 
