@@ -76,9 +76,10 @@ constexpr int64_t kLastLevelCacheBytes = int64_t(256) << 20;
 bool stream_rows(const pkv_pool *p, int32_t batch, int32_t max_len) {
   if (p->load_policy == PKV_LOAD_STREAM) return true;
   if (p->load_policy == PKV_LOAD_CACHED) return false;
-  const int64_t row = (int64_t)p->n_kv_heads * (p->head_dim + v_dim(p)) *
-                      (int64_t)dtype_bytes(p->dtype);
-  return batch == 1 && p->n_layers * (int64_t)max_len * row > kLastLevelCacheBytes;
+  // in double: no field combination can overflow the product
+  const double row = (double)p->n_kv_heads * ((double)p->head_dim + v_dim(p)) *
+                     (double)dtype_bytes(p->dtype);
+  return batch == 1 && (double)p->n_layers * max_len * row > (double)kLastLevelCacheBytes;
 }
 
 // The table fields every gathering kernel takes.
