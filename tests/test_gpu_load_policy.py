@@ -10,8 +10,9 @@ the load kind is a cache hint only, so
     with the rotary turn folded in)
 
 are the same bits under both policies, on ragged and single requests,
-16-token pages and MLA-shaped keys (192 wide, values 128); the streamed
-output meets the CPU fp64 oracle at the bf16 tolerance; and the headline
+16-token pages, MLA-shaped keys (192 wide, values 128) and an fp32 pool of
+64-wide rows (whose vector kernels ignore the policy); the streamed output
+meets the CPU fp64 oracle at the pool dtype's tolerance; and the headline
 shape (one request of 32768 keys on a 32-layer pool), where PKV_LOAD_AUTO
 streams, gives the bits of PKV_LOAD_CACHED."""
 
@@ -42,6 +43,9 @@ CASES = {
                                             head_dim=128, dtype="bf16"), 5),
     "mla": (lambda: W.random_case(1203, [300, 77], n_heads=16, n_kv_heads=16, head_dim=192,
                                   v_head_dim=128, dtype="bf16"), 4),
+    # the vector kernels (fp32, head_dim 64) read cached under every policy
+    "f32_d64": (lambda: W.random_case(1204, [5, 130, 999], n_heads=8, n_kv_heads=2, head_dim=64,
+                                      dtype="f32"), 6),
 }
 
 
@@ -72,8 +76,9 @@ def run(case, form, policy, ns):
     return res, t, out
 
 
-# the rotary step takes 128-wide keys and values only: no MLA-shaped case
-PAIRS = [(n, f) for n in CASES for f in ("split", "store", "rope") if not (n == "mla" and f == "rope")]
+# the rotary step takes bf16 pools with 128-wide keys and values only
+PAIRS = [(n, f) for n in CASES for f in ("split", "store", "rope")
+         if not (n in ("mla", "f32_d64") and f == "rope")]
 
 
 @pytest.mark.parametrize("name,form", PAIRS)
@@ -104,7 +109,7 @@ def test_streamed_rows_give_the_bits_of_cached_rows(name, form):
                               to_np(t["k_new"]), to_np(t["v_new"]))
             ref = OP.decode(kb, vb, 0, case.req_to_token, case.page_size, case.req_pool_indices,
                             case.seq_lens, to_np(t["q"]), case.sm_scale)
-        assert_close(to_np(out), ref, "bf16", f"{name} streamed store step vs oracle")
+        assert_close(to_np(out), ref, case.dtype, f"{name} streamed store step vs oracle")
 
 
 def test_auto_policy_at_the_headline_shape():
