@@ -12,24 +12,37 @@ import torch
 import oracle
 import workloads as W
 from paged_kv_attention_12_amd import api
+from paged_kv_attention_12_amd import binding as B
 from tests.gpu_util import assert_close, say, to_np
 
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("shape", ["three_requests", "one_request_streamed"])
 @pytest.mark.parametrize("form", ["rope_then_step", "rope_in_step"])
-def test_graph_captured_decode_loop_advances_metadata_in_place(form):
+def test_graph_captured_decode_loop_advances_metadata_in_place(form, shape):
     """rope_then_step: the rotary write, then split attention and merge;
     rope_in_step: the rotary turn folded into the split kernel
-    (pkv_paged_decode_rope_store), then the merge."""
+    (pkv_paged_decode_rope_store), then the merge.  one_request_streamed: a
+    single request of ~3000 keys on a 32-layer pool, whose K/V over all
+    layers exceed the last-level cache, so the default load policy reads its
+    rows with non-temporal loads (checked with pkv_decode_load_kind)."""
     steps = 6
-    start = np.array([300, 451, 17], dtype=np.int32)      # position of each request's first token
+    if shape == "three_requests":
+        start = np.array([300, 451, 17], dtype=np.int32)   # position of each request's first token
+        n_layers = 1
+    else:
+        start = np.array([2990], dtype=np.int32)
+        n_layers = 32
     H, Hk, d = 32, 8, 128
     # table rows hold every position the loop reaches, including the one the
     # last metadata advance looks up (start + steps)
     case = W.random_case(960, list(start + steps + 1), n_heads=H, n_kv_heads=Hk, head_dim=d,
-                         dtype="bf16")
+                         dtype="bf16", n_layers=n_layers)
     t = W.make_tensors(case, device="cuda", poison=False)
+    pool = B.make_pool(t["k_buffer"], t["v_buffer"], t["req_to_token"])
+    streamed = B.pkv_decode_load_kind(pool, case.batch, int((start + steps).max()))
+    assert streamed == (1 if shape == "one_request_streamed" else 0)
     B_ = case.batch
     rpi = case.req_pool_indices
     # the first step: each request's token at position start_b (seq_len start_b + 1); the host
@@ -82,7 +95,7 @@ def test_graph_captured_decode_loop_advances_metadata_in_place(form):
         for x in (q, k_new, v_new):
             x.copy_(torch.randn(x.shape, generator=gen, device="cuda"))
         q0, kn0, vn0 = to_np(q), to_np(k_new), to_np(v_new)
-        say("graph loop step", form, k)
+        say("graph loop step", form, shape, k)
         g.replay()
         torch.cuda.synchronize()
         pos = start + k
