@@ -168,6 +168,30 @@ def test_decode_deterministic_and_slot_permutation_invariant():
     assert torch.equal(o1, o3)
 
 
+def test_prefill_deterministic_and_slot_permutation_invariant():
+    """Ragged causal prefill (with its K/V write): the same bits on a second
+    run, and the same bits after every slot of the pool moves to pi[slot]
+    with the table rewritten the same way (keys are taken in logical order;
+    the write slots follow the table)."""
+    case = W.random_case(16, [700, 130, 1500], [300, 130, 257], n_heads=32, n_kv_heads=8,
+                         head_dim=128, dtype="bf16", size=4096)
+    t = W.make_tensors(case, device="cuda")
+    pi = np.random.default_rng(1).permutation(case.size)
+    pi_t = torch.from_numpy(pi).cuda()
+    kb = torch.empty_like(t["k_buffer"])
+    vb = torch.empty_like(t["v_buffer"])
+    kb[:, pi_t] = t["k_buffer"]
+    vb[:, pi_t] = t["v_buffer"]
+    o1 = gpu_prefill(case, t).clone()
+    o2 = gpu_prefill(case, t).clone()
+    assert torch.equal(o1, o2)
+    case2 = W.Case(**{**case.__dict__, "req_to_token": pi[case.req_to_token].astype(np.int32)})
+    t2 = dict(t, k_buffer=kb, v_buffer=vb,
+              req_to_token=torch.from_numpy(case2.req_to_token).cuda())
+    o3 = gpu_prefill(case2, t2)
+    assert torch.equal(o1, o3)
+
+
 def test_decode_split_counts_all_match_oracle():
     case = W.random_case(12, [4000, 1234, 17], n_heads=32, n_kv_heads=8, head_dim=128,
                          dtype="bf16")
